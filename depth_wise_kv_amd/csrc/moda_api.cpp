@@ -1,0 +1,220 @@
+// C ABI of libmoda (declared in include/moda.h): host-side validation,
+// kernel selection and launch.  No device memory is allocated here.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moda.h"
+#include "moda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moda_status fail(moda_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+moda_status ok() {
+  g_last_error.clear();
+  return MODA_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 62;
+
+// a * b * ... without overflow past kMaxElems; returns -1 on overflow
+int64_t checked_prod(std::initializer_list<int64_t> xs) {
+  int64_t acc = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && acc > kMaxElems / x) return -1;
+    acc *= x;
+  }
+  return acc;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+moda_status check_shape_impl(const moda_shape *s) {
+  if (!s) return fail(MODA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 1 || s->Hq < 1 || s->Hkv < 1 || s->T < 1)
+    return fail(MODA_ERR_INVALID_ARG, "B, Hq, Hkv and T must be >= 1");
+  if (s->L < 0) return fail(MODA_ERR_INVALID_ARG, "L must be >= 0");
+  if (s->Hq % s->Hkv != 0) return fail(MODA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+  if (s->dtype != MODA_F32 && s->dtype != MODA_BF16)
+    return fail(MODA_ERR_INVALID_ARG, "dtype must be MODA_F32 or MODA_BF16");
+  if (s->d != 32 && s->d != 64 && s->d != 128)
+    return fail(MODA_ERR_UNSUPPORTED, "head dim d must be 32, 64 or 128");
+  if (s->dtype == MODA_BF16 && s->d == moda::kMfmaD && s->Hq / s->Hkv > moda::kMfmaRows)
+    return fail(MODA_ERR_UNSUPPORTED, "bf16 with d = 128 supports G = Hq / Hkv up to 128");
+  if (checked_prod({s->B, s->Hq, s->T, s->d}) < 0 ||
+      checked_prod({s->B, s->Hkv, s->T, s->L, s->d}) < 0 ||
+      checked_prod({s->B, s->Hkv, s->T, s->L, s->d, 4}) < 0)
+    return fail(MODA_ERR_INVALID_ARG, "tensor size overflows");
+  return MODA_OK;
+}
+
+// The MFMA path (and its packed depth layout) serves every bf16 shape with
+// d == 128; the layout does not depend on G, so a cache can be packed
+// without knowing the query head count.
+bool use_mfma(const moda_shape *s) { return s->dtype == MODA_BF16 && s->d == moda::kMfmaD; }
+
+int64_t depth_blocks(const moda_shape *s) {
+  return (s->T * s->L + moda::kDepthBlock - 1) / moda::kDepthBlock;
+}
+
+size_t cache_bytes(const moda_shape *s) {
+  if (s->L == 0) return 0;
+  if (use_mfma(s)) return (size_t)(s->B * s->Hkv * depth_blocks(s) * moda::kPackedBlockBytes);
+  const int64_t es = s->dtype == MODA_BF16 ? 2 : 4;
+  return (size_t)(2 * s->B * s->Hkv * s->T * s->L * s->d * es);
+}
+
+moda_status grid_fits(const moda_shape *s) {
+  int64_t grid;
+  if (use_mfma(s)) {
+    const int64_t G = s->Hq / s->Hkv, tq = moda::kMfmaRows / G;
+    grid = (s->T + tq - 1) / tq * s->B * s->Hkv;
+    if (s->L > 0 && depth_blocks(s) > 0x7FFFFFFFll)
+      return fail(MODA_ERR_UNSUPPORTED, "depth cache too long for the pack grid");
+    if (s->B * s->Hkv > 65535) return fail(MODA_ERR_UNSUPPORTED, "B * Hkv above 65535");
+  } else {
+    grid = s->B * s->Hq * s->T;
+  }
+  if (grid > 0x7FFFFFFFll) return fail(MODA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return MODA_OK;
+}
+
+moda_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(MODA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+moda::FwdArgs make_fwd_args(const moda_shape *s, const void *q, const void *k, const void *v,
+                            const void *packed, void *out, float *lse, bool has_depth) {
+  moda::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.packed = packed;
+  a.out = out;
+  a.lse = lse;
+  a.B = s->B;
+  a.Hq = s->Hq;
+  a.Hkv = s->Hkv;
+  a.T = s->T;
+  a.L = has_depth ? s->L : 0;
+  a.d = s->d;
+  a.nblk = depth_blocks(s);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
+  a.has_depth = has_depth && s->L > 0;
+  return a;
+}
+
+moda_status check_qkvo(const void *q, const void *k, const void *v, const void *out,
+                       const float *lse) {
+  if (!q || !k || !v || !out) return fail(MODA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (lse && !aligned16(lse)))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  return MODA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moda_status moda_check_shape(const moda_shape *s) {
+  moda_status st = check_shape_impl(s);
+  if (st != MODA_OK) return st;
+  st = grid_fits(s);
+  if (st != MODA_OK) return st;
+  return ok();
+}
+
+size_t moda_depth_cache_bytes(const moda_shape *s) {
+  if (check_shape_impl(s) != MODA_OK) return 0;
+  return cache_bytes(s);
+}
+
+const char *moda_fwd_variant(const moda_shape *s) {
+  if (check_shape_impl(s) != MODA_OK) return "";
+  return use_mfma(s) ? "mfma_bf16_d128" : "generic";
+}
+
+moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth, const void *v_depth,
+                                  void *packed, size_t packed_bytes, void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_pack_depth_cache needs L >= 1");
+  if (!k_depth || !v_depth || !packed)
+    return fail(MODA_ERR_INVALID_ARG, "k_depth, v_depth and packed must be non-NULL");
+  if (!aligned16(k_depth) || !aligned16(v_depth) || !aligned16(packed))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t need = cache_bytes(s);
+  if (packed_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(packed_bytes));
+  moda::PackArgs a{k_depth, v_depth, packed, s->B, s->Hkv, s->T, s->L, s->d, depth_blocks(s)};
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (use_mfma(s)) return hip_status(moda::launch_pack_mfma(a, stream), "pack launch");
+  return hip_status(moda::launch_pack_generic(a, s->dtype == MODA_BF16, stream), "pack launch");
+}
+
+moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
+                     const void *packed, size_t packed_bytes, void *out, float *lse,
+                     void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  st = check_qkvo(q, k, v, out, lse);
+  if (st != MODA_OK) return st;
+  if (s->L > 0) {
+    if (!packed) return fail(MODA_ERR_INVALID_ARG, "packed must be non-NULL when L > 0");
+    if (!aligned16(packed)) return fail(MODA_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+    const size_t need = cache_bytes(s);
+    if (packed_bytes < need)
+      return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
+                                            " bytes, got " + std::to_string(packed_bytes));
+  } else if (packed || packed_bytes) {
+    return fail(MODA_ERR_INVALID_ARG, "packed must be NULL with size 0 when L == 0");
+  }
+  moda::FwdArgs a = make_fwd_args(s, q, k, v, packed, out, lse, true);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (use_mfma(s))
+    return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), stream), "fwd launch");
+  return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "fwd launch");
+}
+
+moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
+                            void *out, float *lse, void *hip_stream) {
+  if (!s) return fail(MODA_ERR_INVALID_ARG, "shape is NULL");
+  moda_shape s0 = *s;
+  s0.L = 0;
+  moda_status st = moda_check_shape(&s0);
+  if (st != MODA_OK) return st;
+  st = check_qkvo(q, k, v, out, lse);
+  if (st != MODA_OK) return st;
+  moda::FwdArgs a = make_fwd_args(&s0, q, k, v, nullptr, out, lse, false);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (use_mfma(&s0))
+    return hip_status(moda::launch_fwd_mfma(a, (int)(s0.Hq / s0.Hkv), stream), "causal launch");
+  return hip_status(moda::launch_fwd_generic(a, s0.dtype == MODA_BF16, stream), "causal launch");
+}
+
+const char *moda_status_string(moda_status st) {
+  switch (st) {
+    case MODA_OK: return "MODA_OK";
+    case MODA_ERR_INVALID_ARG: return "MODA_ERR_INVALID_ARG";
+    case MODA_ERR_UNSUPPORTED: return "MODA_ERR_UNSUPPORTED";
+    case MODA_ERR_HIP: return "MODA_ERR_HIP";
+  }
+  return "MODA_ERR_UNKNOWN";
+}
+
+const char *moda_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

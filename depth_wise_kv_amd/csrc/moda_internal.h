@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI layer (moda_api.cpp) and the HIP
+// kernels (moda_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace moda {
+
+// Geometry of the MFMA path (bf16, head dim 128).
+constexpr int kMfmaD = 128;         // head dimension
+constexpr int kMfmaRows = 128;      // query rows (token x head pairs) per workgroup
+constexpr int kDepthBlock = 32;     // depth entries per packed block
+constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part + V part
+
+struct FwdArgs {
+  const void *q, *k, *v, *packed;
+  void *out;
+  float *lse;
+  int64_t B, Hq, Hkv, T, L, d;
+  int64_t nblk;   // packed depth blocks per (b, kv head) (MFMA path)
+  float scale_log2;  // log2(e) / sqrt(d)
+  bool has_depth;
+};
+
+struct PackArgs {
+  const void *kd, *vd;
+  void *packed;
+  int64_t B, Hkv, T, L, d;
+  int64_t nblk;
+};
+
+// MFMA path: dtype bf16, d == 128, G divides 32.
+hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s);
+hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
+
+// Generic path: fp32 or bf16, d in {32, 64, 128}, any G.
+hipError_t launch_fwd_generic(const FwdArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_pack_generic(const PackArgs &a, bool bf16, hipStream_t s);
+
+}  // namespace moda

@@ -1,0 +1,582 @@
+// HIP kernels of the MoDA forward for gfx950 (MI355X).
+//
+// What is computed (hyper.ai page on arXiv 2603.15619, section
+// "Mixture-of-Depths Attention (MoDA)"): each query row (b, h, t) takes one
+// softmax, scaled by 1/sqrt(d), over the causal sequence keys 0..t of KV head
+// h / G and over its own token's L depth keys, and returns the weighted sum
+// of the matching values.  Sequence and depth logits update one online-softmax
+// state; the output is normalised once at the end (section
+// "Hardware-efficient implementation").
+//
+// Kernels:
+//   moda_fwd_mfma   bf16, d = 128.  A workgroup owns 128 query rows made of
+//                   128/G tokens x the G heads of one KV group, so one K/V
+//                   tile in LDS and one depth span serve all G heads (the
+//                   group-aware indexing of the same section).  QK^T and PV
+//                   run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//   moda_pack_mfma  repacks [B,Hkv,T,L,d] depth K/V into 32-entry blocks laid
+//                   out in MFMA operand order, K block then V block, so each
+//                   wave streams its depth span with fully contiguous loads.
+//   moda_fwd_generic / moda_copy_generic: plain VALU path for fp32 inputs and
+//                   shapes the MFMA path does not cover.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moda_internal.h"
+
+namespace moda {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return float_to_bf16_bits(lo) | (float_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_swap32(float x) {
+  // value held by lane (l ^ 32)
+  return __shfl_xor(x, 32, 64);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path geometry.
+//
+// 32x32x16 bf16 MFMA operand/result layout used below (lane l, h = l / 32):
+//   A operand: row (l % 32), 8 consecutive k values of lane half h
+//   B operand: column (l % 32), the same 8 k values as A
+//   result   : column (l % 32), register r holds row 8*(r/4) + 4*h + r%4
+// Only the pairing of k between A and B matters for a contraction, so each
+// operand load below picks whichever k order makes its own load contiguous.
+//
+// Scores are computed transposed, S^T = K * Q^T, so a lane owns one query row
+// (column l % 32) and holds that row's scores in registers: row max and row
+// sum are in-lane work plus one exchange with lane l ^ 32.
+// ---------------------------------------------------------------------------
+constexpr int D = kMfmaD;            // 128
+constexpr int M = kMfmaRows;         // 128 query rows per workgroup
+constexpr int NKEY = 64;             // keys per sequence tile
+constexpr int K_STRIDE = D * 2 + 16; // bytes per K row in LDS (16 B pad)
+constexpr int VT_STRIDE = NKEY * 2 + 16;  // bytes per V^T row in LDS
+constexpr int K_BYTES = NKEY * K_STRIDE;  // 17408
+constexpr int VT_BYTES = D * VT_STRIDE;   // 18432
+constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;  // double buffer: 71680
+constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a block
+
+// Position, inside a V^T row of 64 keys, of the group of 4 consecutive keys
+// starting at key 4*g4.  PV consumes keys in k-steps of 16; within k-step kk,
+// lane half h needs keys {16kk+4h+0..3, 16kk+8+4h+0..3} (the keys its S^T
+// registers hold), stored here as 8 contiguous bf16 at 16kk + 8h.
+__device__ __forceinline__ int vt_pos(int g4) {
+  const int kk = g4 >> 2, a = (g4 >> 1) & 1, h = g4 & 1;
+  return 16 * kk + 8 * h + 4 * a;
+}
+
+struct MfmaState {
+  float m;          // running max of scaled logits (log2 units)
+  float lsum;       // this lane's partial sum of 2^(x - m)
+  floatx16 acc[4];  // O^T accumulator: 4 blocks of 32 head-dim rows
+};
+
+// One online-softmax step over a 32-entry score block s (already masked with
+// -inf).  Returns the bf16 B operands for PV in pb[0..1].
+__device__ __forceinline__ void softmax_block(MfmaState &st, const floatx16 &s, float scale_log2,
+                                              bf16x8 *pb) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = fmaxf(mx, wave_swap32(mx));
+  const float m_new = fmaxf(st.m, mx * scale_log2);
+  const float alpha = fast_exp2(st.m - m_new);
+  st.m = m_new;
+  st.lsum *= alpha;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+  float sum = 0.f;
+  u32x4 w[2];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = fast_exp2(fmaf(s[r], scale_log2, -m_new));
+    const float p1 = fast_exp2(fmaf(s[r + 1], scale_log2, -m_new));
+    sum += p0 + p1;
+    w[r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+  }
+  st.lsum += sum;
+  pb[0] = __builtin_bit_cast(bf16x8, w[0]);
+  pb[1] = __builtin_bit_cast(bf16x8, w[1]);
+}
+
+template <bool HAS_DEPTH>
+__global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
+  // A tile holds TQ = floor(128 / G) tokens x G heads; rows past TQ * G idle.
+  const int G = (int)(p.Hq / p.Hkv);
+  const int TQ = M / G;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+
+  const int64_t T = p.T;
+  const int64_t BH = p.B * p.Hkv;
+  const int64_t ntiles = (T + TQ - 1) / TQ;
+  // Heaviest causal tiles first: block 0..BH-1 take the last tile of each head.
+  const int64_t x = blockIdx.x;
+  const int64_t tile = ntiles - 1 - x / BH;
+  const int64_t bh = x % BH;
+  const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int64_t t0 = tile * TQ;
+
+  // This lane's query row: row r = token-in-tile * G + head-in-group.
+  const int r = wave * 32 + li;
+  const bool row_used = r < TQ * G;
+  const int64_t tok = row_used ? t0 + r / G : T;  // idle rows sit past the end
+  const int64_t head = hkv * G + (row_used ? r % G : 0);
+  const bool row_ok = tok < T;
+
+  // Q row as the B operand of S^T = K Q^T: lane half h holds dims 64h..64h+63,
+  // 8 per k-step.
+  bf16x8 qb[8];
+  {
+    const __bf16 *qrow = (const __bf16 *)p.q + ((b * p.Hq + head) * T + (row_ok ? tok : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 u = row_ok ? *(const u32x4 *)(qrow + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+      qb[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  MfmaState st;
+  st.m = -INFINITY;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] = 0.f;
+
+  // ---------------- sequence part: key tiles 0 .. the tile's last token
+  const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
+  const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
+  const int64_t wave_tok_lo = t0 + (wave * 32) / G;
+  const __bf16 *kbase = (const __bf16 *)p.k + bh * T * D;
+  const __bf16 *vbase = (const __bf16 *)p.v + bh * T * D;
+
+  // staging roles: K as 1024 16-byte chunks (4 per thread); V as a 4-key by
+  // 8-dim block per thread, transposed into V^T on the way into LDS.
+  const int v_g4 = tid & 15, v_dg = tid >> 4;
+  u32x4 kreg[4], vreg[4];
+
+  auto gload = [&](int kt) {
+    const int64_t key0 = (int64_t)kt * NKEY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int64_t key = key0 + (c >> 4);
+      kreg[i] = key < T ? *(const u32x4 *)(kbase + key * D + (c & 15) * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t key = key0 + 4 * v_g4 + c;
+      vreg[c] = key < T ? *(const u32x4 *)(vbase + key * D + 8 * v_dg) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto lds_store = [&](int buf) {
+    char *kb = smem + buf * BUF_BYTES;
+    char *vb = kb + K_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4 *)(kb + (c >> 4) * K_STRIDE + (c & 15) * 16) = kreg[i];
+    }
+    const int pos = vt_pos(v_g4);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int w = n >> 1;
+      uint32_t k0 = vreg[0][w], k1 = vreg[1][w], k2 = vreg[2][w], k3 = vreg[3][w];
+      u32x2 out;
+      if (n & 1) {
+        out[0] = (k0 >> 16) | (k1 & 0xFFFF0000u);
+        out[1] = (k2 >> 16) | (k3 & 0xFFFF0000u);
+      } else {
+        out[0] = (k0 & 0xFFFFu) | (k1 << 16);
+        out[1] = (k2 & 0xFFFFu) | (k3 << 16);
+      }
+      *(u32x2 *)(vb + (8 * v_dg + n) * VT_STRIDE + pos * 2) = out;
+    }
+  };
+
+  gload(0);
+  lds_store(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) gload(kt + 1);
+    const char *kb = smem + buf * BUF_BYTES;
+    const char *vb = kb + K_BYTES;
+
+    floatx16 s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[kb2][rr] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = *(const bf16x8 *)(kb + (kb2 * 32 + li) * K_STRIDE + (64 * lh + 8 * ks) * 2);
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kb2], 0, 0, 0);
+      }
+    }
+    const int64_t key0 = (int64_t)kt * NKEY;
+    if (key0 + NKEY - 1 > wave_tok_lo) {  // a key past some row's token: causal mask
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int64_t key = key0 + kb2 * 32 + 8 * (rr >> 2) + 4 * lh + (rr & 3);
+          if (key > tok) s[kb2][rr] = -INFINITY;
+        }
+    }
+    // one online-softmax update over the whole 64-key tile
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb2][rr]);
+    mx = fmaxf(mx, wave_swap32(mx));
+    const float m_new = fmaxf(st.m, mx * p.scale_log2);
+    const float alpha = fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] *= alpha;
+    bf16x8 pb[4];
+    float sum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      u32x4 w[2];
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0 = fast_exp2(fmaf(s[kb2][rr], p.scale_log2, -m_new));
+        const float p1 = fast_exp2(fmaf(s[kb2][rr + 1], p.scale_log2, -m_new));
+        sum += p0 + p1;
+        w[rr >> 3][(rr & 7) >> 1] = pack_bf16x2(p0, p1);
+      }
+      pb[2 * kb2] = __builtin_bit_cast(bf16x8, w[0]);
+      pb[2 * kb2 + 1] = __builtin_bit_cast(bf16x8, w[1]);
+    }
+    st.lsum += sum;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = *(const bf16x8 *)(vb + (32 * nb + li) * VT_STRIDE + (16 * kk + 8 * lh) * 2);
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], st.acc[nb], 0, 0, 0);
+      }
+
+    if (kt + 1 < n_kt) lds_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- depth part: this wave's tokens' contiguous depth span
+  if constexpr (HAS_DEPTH) {
+    const int64_t L = p.L;
+    const int64_t wt_lo = t0 + (wave * 32) / G;
+    int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;  // one past the wave's last token
+    if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
+    if (wt_hi > T) wt_hi = T;
+    if (L > 0 && wt_lo < wt_hi) {
+      const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
+      const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
+      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes;
+      const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
+      for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+        const char *kp = pk + blk * kPackedBlockBytes;
+        const char *vp = kp + BLK_HALF;
+        floatx16 sd;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sd[rr] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kp + (ks * 64 + lane) * 16));
+          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sd, 0, 0, 0);
+        }
+        const int64_t e0 = blk * kDepthBlock;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int64_t e = e0 + 8 * (rr >> 2) + 4 * lh + (rr & 3);
+          if ((uint64_t)(e - my_lo) >= (uint64_t)L) sd[rr] = -INFINITY;
+        }
+        bf16x8 pb[2];
+        softmax_block(st, sd, p.scale_log2, pb);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, *(const u32x4 *)(vp + ((nb * 2 + kk) * 64 + lane) * 16));
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], st.acc[nb], 0, 0, 0);
+          }
+      }
+    }
+  }
+
+  // ---------------- epilogue: the single normalisation
+  const float ltot = st.lsum + wave_swap32(st.lsum);
+  if (row_ok) {
+    const float inv = 1.0f / ltot;
+    __bf16 *orow = (__bf16 *)p.out + ((b * p.Hq + head) * T + tok) * D;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 o;
+        o[0] = pack_bf16x2(st.acc[nb][4 * g + 0] * inv, st.acc[nb][4 * g + 1] * inv);
+        o[1] = pack_bf16x2(st.acc[nb][4 * g + 2] * inv, st.acc[nb][4 * g + 3] * inv);
+        *(u32x2 *)(orow + 32 * nb + 8 * g + 4 * lh) = o;
+      }
+    if (p.lse && lh == 0)
+      p.lse[(b * p.Hq + head) * T + tok] = (st.m + __log2f(ltot)) * 0.69314718055994531f;
+  }
+}
+
+// Depth repack into MFMA operand order.  One workgroup per 32-entry block of
+// the flat (token, entry) axis of one (b, kv head):
+//   K half: 8 k-steps x 64 lanes x 16 B; lane l of k-step ks holds entry
+//           l % 32, dims 64*(l/32) + 8*ks .. +7   (the A operand of S^T = K Q^T)
+//   V half: 4 dim blocks x 2 k-steps x 64 lanes x 16 B; lane l of (nb, kk)
+//           holds dim 32*nb + l%32 of entries 16kk + 8*(j/4) + 4*(l/32) + j%4,
+//           j = 0..7 (the A operand of O^T += V^T P^T)
+// Entries past T*L are zero.
+constexpr int PK_ROW = D * 2 + 16;  // LDS row stride (bytes) while repacking
+
+__global__ __launch_bounds__(256) void moda_pack_mfma(PackArgs p) {
+  __shared__ __attribute__((aligned(16))) char ks_lds[kDepthBlock * PK_ROW];
+  __shared__ __attribute__((aligned(16))) char vs_lds[kDepthBlock * PK_ROW];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int64_t blk = blockIdx.x;
+  const int64_t TL = p.T * p.L;
+  const __bf16 *kd = (const __bf16 *)p.kd + bh * TL * D;
+  const __bf16 *vd = (const __bf16 *)p.vd + bh * TL * D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;  // 512 chunks of 16 B per half
+    const int ent = c >> 4, ch = c & 15;
+    const int64_t e = blk * kDepthBlock + ent;
+    u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+    if (e < TL) {
+      kv = *(const u32x4 *)(kd + e * D + ch * 8);
+      vv = *(const u32x4 *)(vd + e * D + ch * 8);
+    }
+    *(u32x4 *)(ks_lds + ent * PK_ROW + ch * 16) = kv;
+    *(u32x4 *)(vs_lds + ent * PK_ROW + ch * 16) = vv;
+  }
+  __syncthreads();
+  char *dst = (char *)p.packed + (bh * p.nblk + blk) * kPackedBlockBytes;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int o = tid + 256 * i;  // output chunk
+    const int ks = o >> 6, l = o & 63;
+    const u32x4 kv = *(const u32x4 *)(ks_lds + (l & 31) * PK_ROW + (64 * (l >> 5) + 8 * ks) * 2);
+    *(u32x4 *)(dst + o * 16) = kv;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int o = tid + 256 * i;
+    const int nbkk = o >> 6, l = o & 63;
+    const int nb = nbkk >> 1, kk = nbkk & 1;
+    const int n = 32 * nb + (l & 31), hh = l >> 5;
+    uint32_t h16[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ent = 16 * kk + 8 * (j >> 2) + 4 * hh + (j & 3);
+      h16[j] = *(const uint16_t *)(vs_lds + ent * PK_ROW + n * 2);
+    }
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = h16[2 * j] | (h16[2 * j + 1] << 16);
+    *(u32x4 *)(dst + BLK_HALF + o * 16) = w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU path (fp32 inputs, or bf16 shapes outside the MFMA path).
+// One wave per query row.  Each lane keeps its own online-softmax state over
+// a strided subset of the row's entries; the 64 states are merged at the end.
+// Depth is read from the generic packed layout: [Kd natural | Vd natural].
+// ---------------------------------------------------------------------------
+template <typename E>
+__device__ __forceinline__ float load_elem(const E *p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float *p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, int64_t i) {
+  return bf16_bits_to_float(p[i]);
+}
+template <typename E>
+__device__ __forceinline__ void store_elem(E *p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_elem<float>(float *p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, int64_t i, float v) {
+  p[i] = (uint16_t)float_to_bf16_bits(v);
+}
+
+template <typename E, int DG, bool HAS_DEPTH>
+__global__ __launch_bounds__(64) void moda_fwd_generic(FwdArgs p) {
+  __shared__ float qs[DG];
+  __shared__ float red[64][DG + 1];
+  __shared__ float lred[64];
+  __shared__ float mred[64];
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;  // (b, h, t) flattened
+  const int64_t T = p.T;
+  const int64_t t = row % T, h = (row / T) % p.Hq, b = row / (T * p.Hq);
+  const int64_t G = p.Hq / p.Hkv;
+  const int64_t bh = b * p.Hkv + h / G;
+  const E *q = (const E *)p.q + row * DG;
+  const E *k = (const E *)p.k + bh * T * DG;
+  const E *v = (const E *)p.v + bh * T * DG;
+  for (int n = lane; n < DG; n += 64) qs[n] = load_elem(q, n);
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f, o[DG];
+#pragma unroll
+  for (int n = 0; n < DG; ++n) o[n] = 0.f;
+
+  auto visit = [&](const E *kr, const E *vr) {
+    float s = 0.f;
+#pragma unroll
+    for (int n = 0; n < DG; ++n) s = fmaf(qs[n], load_elem(kr, n), s);
+    const float xv = s * p.scale_log2;
+    if (xv > m) {
+      const float a = fast_exp2(m - xv);
+      l *= a;
+#pragma unroll
+      for (int n = 0; n < DG; ++n) o[n] *= a;
+      m = xv;
+    }
+    const float pw = fast_exp2(xv - m);
+    l += pw;
+#pragma unroll
+    for (int n = 0; n < DG; ++n) o[n] = fmaf(pw, load_elem(vr, n), o[n]);
+  };
+
+  for (int64_t j = lane; j <= t; j += 64) visit(k + j * DG, v + j * DG);
+  if (HAS_DEPTH && p.L > 0) {
+    const int64_t L = p.L;
+    const int64_t half = p.B * p.Hkv * T * L * DG;  // elements of Kd
+    const E *kd = (const E *)p.packed + (bh * T + t) * L * DG;
+    const E *vd = (const E *)p.packed + half + (bh * T + t) * L * DG;
+    for (int64_t i = lane; i < L; i += 64) visit(kd + i * DG, vd + i * DG);
+  }
+
+  // merge the 64 lane states
+  mred[lane] = m;
+  __syncthreads();
+  float mall = -INFINITY;
+  for (int i = 0; i < 64; ++i) mall = fmaxf(mall, mred[i]);
+  const float sc = (m == -INFINITY) ? 0.f : fast_exp2(m - mall);
+  lred[lane] = l * sc;
+#pragma unroll
+  for (int n = 0; n < DG; ++n) red[lane][n] = o[n] * sc;
+  __syncthreads();
+  float lall = 0.f;
+  for (int i = 0; i < 64; ++i) lall += lred[i];
+  E *out = (E *)p.out + row * DG;
+  for (int n = lane; n < DG; n += 64) {
+    float acc = 0.f;
+    for (int i = 0; i < 64; ++i) acc += red[i][n];
+    store_elem(out, n, acc / lall);
+  }
+  if (p.lse && lane == 0) p.lse[row] = (mall + log2f(lall)) * 0.69314718055994531f;
+}
+
+// Generic packed layout = Kd then Vd, both in their natural layout.
+__global__ __launch_bounds__(256) void moda_copy_generic(const u32x4 *kd, const u32x4 *vd,
+                                                         u32x4 *dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    dst[i] = kd[i];
+    dst[n16 + i] = vd[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
+  if (G < 1 || G > M) return hipErrorInvalidValue;
+  const int64_t TQ = M / G;
+  const int64_t ntiles = (a.T + TQ - 1) / TQ;
+  const int64_t grid = ntiles * a.B * a.Hkv;
+  if (a.has_depth)
+    hipLaunchKernelGGL((moda_fwd_mfma<true>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((moda_fwd_mfma<false>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s) {
+  dim3 grid((uint32_t)a.nblk, (uint32_t)(a.B * a.Hkv));
+  hipLaunchKernelGGL(moda_pack_mfma, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename E, int DG>
+static hipError_t launch_generic_d(const FwdArgs &a, hipStream_t s) {
+  const int64_t rows = a.B * a.Hq * a.T;
+  if (a.has_depth)
+    hipLaunchKernelGGL((moda_fwd_generic<E, DG, true>), dim3((uint32_t)rows), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((moda_fwd_generic<E, DG, false>), dim3((uint32_t)rows), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_generic(const FwdArgs &a, bool bf16, hipStream_t s) {
+  if (bf16) {
+    switch (a.d) {
+      case 32: return launch_generic_d<uint16_t, 32>(a, s);
+      case 64: return launch_generic_d<uint16_t, 64>(a, s);
+      case 128: return launch_generic_d<uint16_t, 128>(a, s);
+    }
+  } else {
+    switch (a.d) {
+      case 32: return launch_generic_d<float, 32>(a, s);
+      case 64: return launch_generic_d<float, 64>(a, s);
+      case 128: return launch_generic_d<float, 128>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_generic(const PackArgs &a, bool bf16, hipStream_t s) {
+  const int64_t bytes = a.B * a.Hkv * a.T * a.L * a.d * (bf16 ? 2 : 4);
+  const int64_t n16 = bytes / 16;  // d * es is a multiple of 16 for every supported d
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(moda_copy_generic, dim3((uint32_t)blocks), dim3(256), 0, s,
+                     (const u32x4 *)a.kd, (const u32x4 *)a.vd, (u32x4 *)a.packed, n16);
+  return hipGetLastError();
+}
+
+}  // namespace moda

@@ -1,0 +1,202 @@
+"""ctypes binding of libmoda (include/moda.h): argument marshalling only.
+
+Every step of the MoDA forward runs in libmoda's HIP kernels.  PyTorch only
+supplies device memory and the current stream.  The C entry points keep their
+names (``moda_fwd`` ...); ``pack_depth_cache``, ``fwd`` and ``causal_fwd`` are
+conveniences that allocate outputs with torch and call them.
+
+If libmoda.so is missing or cannot be loaded, importing this module raises:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoda.so")
+
+MODA_OK, MODA_ERR_INVALID_ARG, MODA_ERR_UNSUPPORTED, MODA_ERR_HIP = 0, 1, 2, 3
+MODA_F32, MODA_BF16 = 0, 1
+
+# every symbol include/moda.h declares
+EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
+           "moda_causal_fwd", "moda_status_string", "moda_last_error", "moda_fwd_variant")
+
+
+class ModaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("T", ctypes.c_int64), ("L", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+class ModaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({detail})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libmoda.so not built at {LIB_PATH}; run "
+                          "`python -m depth_wise_kv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sp, vp, sz = ctypes.POINTER(ModaShape), ctypes.c_void_p, ctypes.c_size_t
+    lib.moda_check_shape.argtypes = [sp]
+    lib.moda_check_shape.restype = ctypes.c_int
+    lib.moda_depth_cache_bytes.argtypes = [sp]
+    lib.moda_depth_cache_bytes.restype = sz
+    lib.moda_pack_depth_cache.argtypes = [sp, vp, vp, vp, sz, vp]
+    lib.moda_pack_depth_cache.restype = ctypes.c_int
+    lib.moda_fwd.argtypes = [sp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.moda_fwd.restype = ctypes.c_int
+    lib.moda_causal_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+    lib.moda_causal_fwd.restype = ctypes.c_int
+    lib.moda_status_string.argtypes = [ctypes.c_int]
+    lib.moda_status_string.restype = ctypes.c_char_p
+    lib.moda_last_error.argtypes = []
+    lib.moda_last_error.restype = ctypes.c_char_p
+    lib.moda_fwd_variant.argtypes = [sp]
+    lib.moda_fwd_variant.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def make_shape(B, Hq, Hkv, T, L, d, dtype) -> ModaShape:
+    code = {"f32": MODA_F32, "bf16": MODA_BF16, MODA_F32: MODA_F32, MODA_BF16: MODA_BF16}
+    if not isinstance(dtype, (str, int)):
+        dtype = str(dtype).replace("torch.", "")
+        dtype = {"float32": "f32", "bfloat16": "bf16"}.get(dtype, dtype)
+    return ModaShape(int(B), int(Hq), int(Hkv), int(T), int(L), int(d), code[dtype])
+
+
+def _check(status: int, where: str):
+    if status != MODA_OK:
+        detail = lib.moda_last_error().decode() or lib.moda_status_string(status).decode()
+        raise ModaError(status, where, detail)
+
+
+# ---------------------------------------------------------------- C entry points
+
+def _sref(shape):
+    return None if shape is None else ctypes.byref(shape)
+
+
+def moda_check_shape(shape: ModaShape) -> int:
+    return lib.moda_check_shape(_sref(shape))
+
+
+def moda_depth_cache_bytes(shape: ModaShape) -> int:
+    return int(lib.moda_depth_cache_bytes(_sref(shape)))
+
+
+def moda_fwd_variant(shape: ModaShape) -> str:
+    return lib.moda_fwd_variant(_sref(shape)).decode()
+
+
+def moda_pack_depth_cache(shape, k_depth_ptr, v_depth_ptr, packed_ptr, packed_bytes, stream):
+    return lib.moda_pack_depth_cache(_sref(shape), k_depth_ptr, v_depth_ptr, packed_ptr,
+                                     packed_bytes, stream)
+
+
+def moda_fwd(shape, q_ptr, k_ptr, v_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr, stream):
+    return lib.moda_fwd(_sref(shape), q_ptr, k_ptr, v_ptr, packed_ptr, packed_bytes,
+                        out_ptr, lse_ptr, stream)
+
+
+def moda_causal_fwd(shape, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream):
+    return lib.moda_causal_fwd(_sref(shape), q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream)
+
+
+def moda_status_string(status: int) -> str:
+    return lib.moda_status_string(status).decode()
+
+
+def moda_last_error() -> str:
+    return lib.moda_last_error().decode()
+
+
+# ---------------------------------------------------------------- torch conveniences
+
+def _stream_ptr(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def shape_of(q, k, kd=None) -> ModaShape:
+    B, Hq, T, d = q.shape
+    L = 0 if kd is None else kd.shape[3]
+    return make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+
+
+def _check_tensors(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libmoda takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("libmoda takes contiguous tensors")
+
+
+def pack_depth_cache(kd, vd, shape: ModaShape | None = None, out=None):
+    """Repack Kd, Vd [B,Hkv,T,L,d] into a new (or given) uint8 device buffer."""
+    import torch
+    _check_tensors(kd, vd)
+    if shape is None:
+        B, Hkv, T, L, d = kd.shape
+        shape = make_shape(B, Hkv, Hkv, T, L, d, kd.dtype)
+    n = moda_depth_cache_bytes(shape)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=kd.device)
+    _check(moda_pack_depth_cache(shape, _ptr(kd), _ptr(vd), _ptr(out), out.numel(),
+                                 _stream_ptr(kd)), "moda_pack_depth_cache")
+    return out
+
+
+def fwd(q, k, v, packed=None, L: int = 0, *, with_lse: bool = False, out=None, lse=None):
+    """MoDA forward.  ``packed`` comes from pack_depth_cache with the same
+    shape (the Hq of the pack shape does not matter; only B, Hkv, T, L, d)."""
+    import torch
+    _check_tensors(q, k, v, packed)
+    B, Hq, T, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    nbytes = 0 if packed is None else packed.numel() * packed.element_size()
+    _check(moda_fwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(packed), nbytes, _ptr(out), _ptr(lse),
+                    _stream_ptr(q)), "moda_fwd")
+    return (out, lse) if with_lse else out
+
+
+def causal_fwd(q, k, v, *, with_lse: bool = False, out=None, lse=None):
+    """Causal-only attention (the same kernel without the depth part)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, Hq, T, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], T, 0, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(moda_causal_fwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                           _stream_ptr(q)), "moda_causal_fwd")
+    return (out, lse) if with_lse else out
+
+
+def moda_forward(q, k, v, kd=None, vd=None, *, with_lse: bool = False):
+    """Pack (when L > 0) then forward: the whole MoDA path in two launches."""
+    if kd is None or kd.shape[3] == 0:
+        return fwd(q, k, v, None, 0, with_lse=with_lse)
+    B, Hq, T, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], T, kd.shape[3], d, q.dtype)
+    packed = pack_depth_cache(kd, vd, shape)
+    return fwd(q, k, v, packed, kd.shape[3], with_lse=with_lse)

@@ -1,0 +1,127 @@
+/*
+ * moda.h -- C ABI of libmoda: the Mixture-of-Depths Attention (MoDA) forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (hyper.ai page on arXiv 2603.15619, section "Mixture-of-Depths
+ * Attention (MoDA)"; chatpaper.ai abstract): every query row (b, h, t) takes
+ * one softmax, scaled by 1/sqrt(d), over
+ *   - the causal sequence keys K[b, g, j, :] for j = 0..t of the current layer,
+ *   - the token's own L depth keys Kd[b, g, t, i, :], i = 0..L-1, written by
+ *     the preceding layers (same page, section "Depth stream mechanism"),
+ * where g = h / G and G = Hq / Hkv query heads share one KV head (section
+ * "Hardware-efficient implementation" names G the GQA group count).  The
+ * output row is the weight-averaged matching values V and Vd.  Sequence and
+ * depth logits feed one online-softmax state and are normalised once
+ * (section "Hardware-efficient implementation").
+ *
+ * Tensors (all contiguous, row-major, device memory unless stated):
+ *   Q   [B, Hq,  T, d]          element type = shape.dtype
+ *   K,V [B, Hkv, T, d]          element type = shape.dtype
+ *   Kd,Vd [B, Hkv, T, L, d]     element type = shape.dtype
+ *   O   [B, Hq,  T, d]          element type = shape.dtype (bf16: round to
+ *                               nearest even from the fp32 result)
+ *   LSE [B, Hq,  T]   float32   natural-log normaliser of each row (optional)
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller allocates every buffer and keeps it alive until
+ *     the stream has finished the enqueued work.  The library allocates no
+ *     device memory and keeps no pointer after returning.
+ *   - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL is
+ *     the null stream) and the call returns without synchronising.
+ *   - Validation happens on the host before anything is enqueued; on any
+ *     error nothing is enqueued.  Errors are returned as moda_status, never
+ *     by abort or exception; moda_last_error() gives the detail (per thread).
+ *   - Device pointers must be 16-byte aligned.
+ *   - Thread safety: every call is thread-safe.
+ */
+#ifndef MODA_H_
+#define MODA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MODA_OK = 0,
+  MODA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, ... */
+  MODA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head dim) */
+  MODA_ERR_HIP = 3          /* the HIP runtime reported an error */
+} moda_status;
+
+typedef enum { MODA_F32 = 0, MODA_BF16 = 1 } moda_dtype;
+
+/* Problem shape.  Requirements: B, Hq, Hkv, T >= 1; L >= 0; Hq % Hkv == 0;
+ * d in {32, 64, 128}; every tensor has fewer than 2^62 elements. */
+typedef struct {
+  int64_t B, Hq, Hkv, T, L, d;
+  int32_t dtype; /* a moda_dtype */
+} moda_shape;
+
+/* Host-only shape check (no device work).  MODA_OK if every entry point
+ * accepts `s`, otherwise the reason.  Safe to call without a GPU. */
+moda_status moda_check_shape(const moda_shape *s);
+
+/* Bytes the packed depth cache of shape `s` occupies; 0 if `s` is invalid or
+ * has L == 0.  Host only. */
+size_t moda_depth_cache_bytes(const moda_shape *s);
+
+/* Repack the depth stream into the layout moda_fwd streams.
+ *
+ * Passage: hyper.ai page on arXiv 2603.15619, section "Hardware-efficient
+ * implementation": the depth cache is reorganised so that the queries of one
+ * chunk (and all G heads of a KV group) read one contiguous depth span.
+ *
+ *   k_depth, v_depth : Kd, Vd [B, Hkv, T, L, d] (read only)
+ *   packed           : output, packed_bytes >= moda_depth_cache_bytes(s)
+ * The packed format is opaque: a pure function of (shape, library version),
+ * bit-exact copies of the inputs plus zero padding.  Pass the identical
+ * shape to moda_fwd.  Requires L >= 1.
+ */
+moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth,
+                                  const void *v_depth, void *packed,
+                                  size_t packed_bytes, void *hip_stream);
+
+/* MoDA forward: O (and optionally LSE) from Q, the sequence K/V and the
+ * packed depth cache.
+ *
+ * Passage: hyper.ai page on arXiv 2603.15619, sections "Mixture-of-Depths
+ * Attention (MoDA)" and "Hardware-efficient implementation".
+ *
+ *   q, k, v : Q, K, V as above (read only)
+ *   packed  : from moda_pack_depth_cache with the same shape; must be NULL
+ *             (and packed_bytes 0) when L == 0
+ *   out     : O, written in full (no row is left unwritten)
+ *   lse     : NULL, or LSE [B, Hq, T] float32 written in full
+ * With L == 0 the result is causal grouped-query attention.
+ */
+moda_status moda_fwd(const moda_shape *s, const void *q, const void *k,
+                     const void *v, const void *packed, size_t packed_bytes,
+                     void *out, float *lse, void *hip_stream);
+
+/* Causal-only attention: moda_fwd without the depth part (L is ignored).
+ * The in-house FlashAttention-style reference that MoDA is compared with
+ * (the hyper.ai page, section "Main contributions", and the chatpaper.ai
+ * abstract compare MoDA's kernel with FlashAttention-2 at 64K tokens).
+ * Arguments as in moda_fwd. */
+moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k,
+                            const void *v, void *out, float *lse,
+                            void *hip_stream);
+
+/* Static text of a status code (never NULL). */
+const char *moda_status_string(moda_status st);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *moda_last_error(void);
+
+/* Kernel variant moda_fwd would launch for `s` (static text, for logging and
+ * tests): "mfma_bf16_d128", "generic", or "" if `s` is invalid. Host only. */
+const char *moda_fwd_variant(const moda_shape *s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MODA_H_ */

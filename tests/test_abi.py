@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports what include/moda.h declares, and rejects
+bad arguments on the host before touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moda.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    from depth_wise_kv_amd import moda
+    return moda
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(m):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(m.lib, n), f"libmoda.so does not export {n}"
+    assert sorted(m.EXPORTS) == names
+
+
+def shape(m, **kw):
+    base = dict(B=1, Hq=16, Hkv=4, T=4096, L=24, d=128, dtype="bf16")
+    base.update(kw)
+    return m.make_shape(**base)
+
+
+def test_check_shape(m):
+    assert m.moda_check_shape(shape(m)) == m.MODA_OK
+    assert m.moda_check_shape(shape(m, Hq=15)) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_check_shape(shape(m, T=0)) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_check_shape(shape(m, L=-1)) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_check_shape(shape(m, d=96)) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_check_shape(shape(m, Hq=256, Hkv=1)) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_check_shape(shape(m, T=1 << 40, L=1 << 20)) == m.MODA_ERR_INVALID_ARG
+    s = shape(m)
+    s.dtype = 7
+    assert m.moda_check_shape(s) == m.MODA_ERR_INVALID_ARG
+    assert "multiple" in (m.moda_check_shape(shape(m, Hq=15)) and m.moda_last_error())
+
+
+def test_depth_cache_bytes(m):
+    # bf16, d=128: 32-entry blocks of 16 KiB per (b, kv head)
+    assert m.moda_depth_cache_bytes(shape(m)) == 4 * (4096 * 24 // 32) * 16384
+    assert m.moda_depth_cache_bytes(shape(m, T=5, L=3)) == 4 * 1 * 16384
+    assert m.moda_depth_cache_bytes(shape(m, L=0)) == 0
+    # same layout whatever G is
+    assert m.moda_depth_cache_bytes(shape(m, Hq=4)) == m.moda_depth_cache_bytes(shape(m, Hq=32))
+    # generic path: Kd then Vd in natural layout
+    assert m.moda_depth_cache_bytes(shape(m, dtype="f32", d=32, T=64, L=4, Hkv=1, Hq=2)) == \
+        2 * 64 * 4 * 32 * 4
+    assert m.moda_depth_cache_bytes(shape(m, Hq=15)) == 0
+    assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128"
+    assert m.moda_fwd_variant(shape(m, dtype="f32")) == "generic"
+    assert m.moda_fwd_variant(shape(m, d=64)) == "generic"
+
+
+def test_status_strings(m):
+    for st, name in [(0, "MODA_OK"), (1, "MODA_ERR_INVALID_ARG"), (2, "MODA_ERR_UNSUPPORTED"),
+                     (3, "MODA_ERR_HIP")]:
+        assert m.moda_status_string(st) == name
+
+
+def test_fwd_rejects_before_launch(m):
+    """Argument errors return a status without any device call (no GPU here)."""
+    s = shape(m)
+    p = ctypes.c_void_p(4096)       # never dereferenced: validation fails first
+    mis = ctypes.c_void_p(4096 + 8)
+    nb = m.moda_depth_cache_bytes(s)
+    assert m.moda_fwd(s, None, p, p, p, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd(s, mis, p, p, p, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert "aligned" in m.moda_last_error()
+    assert m.moda_fwd(s, p, p, p, None, 0, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd(s, p, p, p, p, nb - 1, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert "too small" in m.moda_last_error()
+    s0 = shape(m, L=0)
+    assert m.moda_fwd(s0, p, p, p, p, 16, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd(shape(m, d=96), p, p, p, p, nb, p, None, None) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_causal_fwd(s, p, None, p, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_causal_fwd(None, p, p, p, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_pack_depth_cache(s, p, p, p, nb - 16, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_pack_depth_cache(s0, p, p, p, 0, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_pack_depth_cache(s, p, None, p, nb, None) == m.MODA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors(m):
+    import torch
+    q = torch.zeros(1, 2, 4, 32)
+    with pytest.raises(ValueError):
+        m.fwd(q, q[:, :1], q[:, :1])

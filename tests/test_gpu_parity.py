@@ -1,0 +1,269 @@
+"""GPU parity: libmoda (through its C ABI) against the fp64 oracle, plus
+invariants that need no oracle.  Runs only on an MI355X (pytest -m gpu).
+
+Tolerances (max-abs on O over every checked element): 1e-5 for fp32 inputs,
+2e-2 for bf16 inputs with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (BF16_TOL, F32_TOL, LSE_TOL_BF16, LSE_TOL_F32, device_case, gather_rows,
+                      host_case, max_err, oracle_rows_from_device, out_to_f64, sample_rows, to_np)
+from synth import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def m():
+    from depth_wise_kv_amd import moda
+    return moda
+
+
+def run_full(m, d_in, L, with_lse=True):
+    kd, vd = (d_in["kd"], d_in["vd"]) if L else (None, None)
+    out, lse = m.moda_forward(d_in["q"], d_in["k"], d_in["v"], kd, vd, with_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_full(m, cfg, dev, tol=None, lse_tol=None):
+    h_in, d_in = host_case(cfg, dev)
+    out, lse = run_full(m, d_in, cfg["L"])
+    L = cfg["L"]
+    ref, rlse = oracle.moda_forward(h_in["q"], h_in["k"], h_in["v"],
+                                    h_in["kd"] if L else None, h_in["vd"] if L else None)
+    f32 = cfg["dtype"] == "f32"
+    tol = tol or (F32_TOL if f32 else BF16_TOL)
+    lse_tol = lse_tol or (LSE_TOL_F32 if f32 else LSE_TOL_BF16)
+    e_o = max_err(out_to_f64(out), ref)
+    e_l = max_err(lse.cpu().numpy(), rlse)
+    print(f"[parity] {cfg} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= tol, f"O error {e_o} > {tol}"
+    assert e_l <= lse_tol, f"LSE error {e_l} > {lse_tol}"
+    return out, lse
+
+
+def shape_cfg(B, Hq, Hkv, T, L, d=128, dtype="bf16", scale=1.0, seed=7):
+    return dict(B=B, Hq=Hq, Hkv=Hkv, T=T, L=L, d=d, dtype=dtype, scale=scale, seed=seed)
+
+
+# ------------------------------------------------------------------ full-oracle parity
+
+def test_tiny_workload_fp32(m, dev):
+    """B1 Hq2 Hkv1 T64 d32 L4, fp32 (generic path), whole tensor."""
+    check_full(m, WORKLOADS["tiny"], dev)
+
+
+MFMA_SHAPES = [
+    # (B, Hq, Hkv, T, L): ragged T, L in {0,1,3,24}, G in {1,2,3,4,8,16,24,32}
+    (1, 2, 1, 1, 0), (1, 2, 1, 1, 3), (1, 4, 1, 17, 1), (1, 4, 2, 129, 3),
+    (2, 8, 2, 1000, 24), (1, 16, 4, 200, 0), (1, 3, 1, 50, 5), (1, 4, 4, 77, 2),
+    (1, 32, 2, 130, 4), (1, 64, 2, 40, 3), (1, 24, 1, 33, 2), (1, 8, 1, 300, 40),
+    (1, 16, 4, 64, 32), (2, 4, 1, 65, 7),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", MFMA_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in MFMA_SHAPES])
+def test_mfma_path_small(m, dev, B, Hq, Hkv, T, L):
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=11 + T + 7 * L)
+    assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) == "mfma_bf16_d128"
+    check_full(m, cfg, dev)
+
+
+GENERIC_SHAPES = [
+    (1, 2, 1, 64, 4, 32, "f32"), (1, 4, 2, 33, 3, 64, "f32"), (2, 4, 1, 70, 0, 128, "f32"),
+    (1, 6, 2, 130, 5, 64, "bf16"), (1, 2, 2, 45, 2, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L,d,dt", GENERIC_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}d{d}{dt}" for b, hq, hk, t, l, d, dt
+                              in GENERIC_SHAPES])
+def test_generic_path(m, dev, B, Hq, Hkv, T, L, d, dt):
+    cfg = shape_cfg(B, Hq, Hkv, T, L, d=d, dtype=dt, seed=3 + T)
+    assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, d, dt)) == "generic"
+    check_full(m, cfg, dev)
+
+
+def test_layer_1p5b_full(m, dev):
+    """B2 Hq16 Hkv4 T4096 d128 L24, bf16 N(0,1)*0.5: every row against the oracle."""
+    cfg = WORKLOADS["layer_1p5b"]
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, cfg["L"])
+    ref, rlse = oracle.moda_forward(*(to_np(d_in[n]) for n in ("q", "k", "v", "kd", "vd")))
+    e_o, e_l = max_err(out_to_f64(out), ref), max_err(lse.cpu().numpy(), rlse)
+    print(f"[parity] layer_1p5b max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
+def sampled_check(m, cfg, dev, n_random=64):
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, cfg["L"])
+    rows = sample_rows(cfg, n_random=n_random, seed=cfg["seed"])
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    got = out_to_f64(gather_rows(out, rows))
+    got_l = gather_rows(lse, rows).cpu().numpy()
+    e_o, e_l = max_err(got, ref), max_err(got_l, rlse)
+    print(f"[parity] {cfg.get('name', cfg)} rows={len(rows)} max|dO|={e_o:.3e} "
+          f"max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    del d_in, out, lse
+    torch.cuda.empty_cache()
+
+
+def test_long_64k_sampled(m, dev):
+    """B1 Hq16 Hkv4 T65536 d128 L32: 73 sampled rows per head."""
+    sampled_check(m, WORKLOADS["long_64k"], dev)
+
+
+def test_depth_heavy_sampled(m, dev):
+    """B4 Hq32 Hkv8 T8192 d128 L128: 73 sampled rows per (b, head)."""
+    sampled_check(m, WORKLOADS["depth_heavy"], dev)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_l0_equals_causal_bitwise(m, dev):
+    cfg = shape_cfg(1, 16, 4, 1000, 0, seed=5)
+    _, d_in = host_case(cfg, dev)
+    o1, l1 = m.fwd(d_in["q"], d_in["k"], d_in["v"], None, 0, with_lse=True)
+    o2, l2 = m.causal_fwd(d_in["q"], d_in["k"], d_in["v"], with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_causal_mode_ignores_depth(m, dev):
+    """moda_causal_fwd on a shape with L > 0 equals causal attention (oracle, L=0)."""
+    cfg = shape_cfg(1, 8, 2, 257, 0, seed=9)
+    h_in, d_in = host_case(cfg, dev)
+    shape = m.make_shape(1, 8, 2, 257, 5, 128, "bf16")
+    out = torch.empty_like(d_in["q"])
+    st = m.moda_causal_fwd(shape, m._ptr(d_in["q"]), m._ptr(d_in["k"]), m._ptr(d_in["v"]),
+                           m._ptr(out), None, m._stream_ptr(out))
+    assert st == m.MODA_OK
+    torch.cuda.synchronize()
+    ref, _ = oracle.moda_forward(h_in["q"], h_in["k"], h_in["v"])
+    assert max_err(out_to_f64(out), ref) <= BF16_TOL
+
+
+def test_deterministic(m, dev):
+    cfg = shape_cfg(2, 8, 2, 777, 9, seed=13)
+    _, d_in = host_case(cfg, dev)
+    o1, l1 = run_full(m, d_in, 9)
+    o2, l2 = run_full(m, d_in, 9)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_all_ones_values(m, dev):
+    """Weights sum to one: V = Vd = 1 gives O = 1 (within bf16 rounding)."""
+    cfg = shape_cfg(1, 8, 2, 300, 6, seed=17)
+    _, d_in = host_case(cfg, dev)
+    d_in["v"].fill_(1.0)
+    d_in["vd"].fill_(1.0)
+    out, _ = run_full(m, d_in, 6)
+    assert float((out.float() - 1.0).abs().max()) <= BF16_TOL
+
+
+def test_depth_permutation(m, dev):
+    cfg = shape_cfg(1, 8, 2, 150, 7, seed=19)
+    _, d_in = host_case(cfg, dev)
+    o1, _ = run_full(m, d_in, 7)
+    perm = torch.randperm(7, generator=torch.Generator().manual_seed(3)).to(dev)
+    d_in["kd"] = d_in["kd"][:, :, :, perm].contiguous()
+    d_in["vd"] = d_in["vd"][:, :, :, perm].contiguous()
+    o2, _ = run_full(m, d_in, 7)
+    assert float((o1.float() - o2.float()).abs().max()) <= BF16_TOL
+
+
+def test_locality_bitwise(m, dev):
+    """Row t ignores keys after t and other tokens' depth entries, exactly."""
+    cfg = shape_cfg(1, 8, 2, 200, 4, seed=23)
+    _, d_in = host_case(cfg, dev)
+    o1, l1 = run_full(m, d_in, 4)
+    t = 97
+    d_in["k"][:, :, t + 1:] += 3.0
+    d_in["v"][:, :, t + 1:] -= 2.0
+    keep_kd, keep_vd = d_in["kd"][:, :, t].clone(), d_in["vd"][:, :, t].clone()
+    d_in["kd"].mul_(-1.5)
+    d_in["vd"].add_(4.0)
+    d_in["kd"][:, :, t] = keep_kd
+    d_in["vd"][:, :, t] = keep_vd
+    o2, l2 = run_full(m, d_in, 4)
+    assert torch.equal(o1[:, :, t], o2[:, :, t]) and torch.equal(l1[:, :, t], l2[:, :, t])
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 32)])
+def test_guard_bands(m, dev, dt, d):
+    """Every output row is written and nothing outside the output is touched."""
+    cfg = shape_cfg(1, 4, 2, 131, 3, d=d, dtype=dt, seed=29)
+    _, d_in = host_case(cfg, dev)
+    n = d_in["q"].numel()
+    pad = 1024
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=d_in["q"].dtype, device=dev)
+    out = buf[pad:pad + n].view_as(d_in["q"])
+    lbuf = torch.full((4 * 131 + 2 * 64,), float("nan"), dtype=torch.float32, device=dev)
+    lse = lbuf[64:64 + 4 * 131].view(1, 4, 131)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"])
+    m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, 3, out=out, lse=lse, with_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+    assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all()
+    assert torch.isnan(lbuf[:64]).all() and torch.isnan(lbuf[64 + 4 * 131:]).all()
+
+
+def unpack_mfma(packed, B, Hkv, T, L):
+    """Invert the bf16/d=128 packed layout on the host (uint16 bit patterns)."""
+    nblk = (T * L + 31) // 32
+    P = to_np(packed).view(np.uint16).reshape(B * Hkv, nblk, 2, 4096)
+    K = P[:, :, 0].reshape(B * Hkv, nblk, 8, 2, 32, 8)        # ks, lh, li, j
+    K = K.transpose(0, 1, 4, 3, 2, 5).reshape(B * Hkv, nblk * 32, 128)
+    V = P[:, :, 1].reshape(B * Hkv, nblk, 4, 2, 2, 32, 2, 4)  # nb, kk, lh, li, ja, jc
+    V = V.transpose(0, 1, 3, 6, 4, 7, 2, 5).reshape(B * Hkv, nblk * 32, 128)
+    return K, V
+
+
+@pytest.mark.parametrize("T,L", [(37, 3), (64, 32), (5, 1), (100, 24)])
+def test_repack_round_trip(m, dev, T, L):
+    cfg = shape_cfg(2, 4, 2, T, L, seed=31 + T)
+    h_in, d_in = host_case(cfg, dev)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"])
+    torch.cuda.synchronize()
+    K, V = unpack_mfma(packed, 2, 2, T, L)
+    TL = T * L
+    assert np.array_equal(K[:, :TL], h_in["kd"].reshape(4, TL, 128))
+    assert np.array_equal(V[:, :TL], h_in["vd"].reshape(4, TL, 128))
+    assert not K[:, TL:].any() and not V[:, TL:].any()
+
+
+def test_generic_repack_round_trip(m, dev):
+    cfg = shape_cfg(1, 2, 1, 19, 3, d=32, dtype="f32", seed=37)
+    h_in, d_in = host_case(cfg, dev)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"])
+    torch.cuda.synchronize()
+    raw = to_np(packed).view(np.float32)
+    n = h_in["kd"].size
+    assert np.array_equal(raw[:n], h_in["kd"].ravel()) and np.array_equal(raw[n:], h_in["vd"].ravel())
+
+
+def test_runs_on_nondefault_stream(m, dev):
+    cfg = shape_cfg(1, 8, 2, 333, 5, seed=41)
+    h_in, d_in = host_case(cfg, dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = m.moda_forward(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                  with_lse=True)
+    s.synchronize()
+    ref, _ = oracle.moda_forward(h_in["q"], h_in["k"], h_in["v"], h_in["kd"], h_in["vd"])
+    assert max_err(out_to_f64(out), ref) <= BF16_TOL
