@@ -44,6 +44,7 @@ moda_status check_shape_impl(const moda_shape *s) {
   if (s->B < 1 || s->Hq < 1 || s->Hkv < 1 || s->T < 1)
     return fail(MODA_ERR_INVALID_ARG, "B, Hq, Hkv and T must be >= 1");
   if (s->L < 0) return fail(MODA_ERR_INVALID_ARG, "L must be >= 0");
+  if (s->L > ((int64_t)1 << 30)) return fail(MODA_ERR_UNSUPPORTED, "L above 2^30");
   if (s->Hq % s->Hkv != 0) return fail(MODA_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
   if (s->dtype != MODA_F32 && s->dtype != MODA_BF16)
     return fail(MODA_ERR_INVALID_ARG, "dtype must be MODA_F32 or MODA_BF16");

@@ -66,60 +66,93 @@ __device__ __forceinline__ float wave_swap32(float x) {
 // (column l % 32) and holds that row's scores in registers: row max and row
 // sum are in-lane work plus one exchange with lane l ^ 32.
 // ---------------------------------------------------------------------------
-constexpr int D = kMfmaD;            // 128
-constexpr int M = kMfmaRows;         // 128 query rows per workgroup
-constexpr int NKEY = 64;             // keys per sequence tile
-constexpr int K_STRIDE = D * 2 + 16; // bytes per K row in LDS (16 B pad)
-constexpr int VT_STRIDE = NKEY * 2 + 16;  // bytes per V^T row in LDS
+constexpr int D = kMfmaD;             // 128
+constexpr int M = kMfmaRows;          // 128 query rows per workgroup
+constexpr int NKEY = 64;              // keys per sequence tile
+constexpr int K_STRIDE = D * 2 + 16;  // bytes per K row in LDS: conflict-free ds_read_b128
+constexpr int V_STRIDE = D * 2 + 64;  // bytes per V row in LDS: conflict-free transpose reads
 constexpr int K_BYTES = NKEY * K_STRIDE;  // 17408
-constexpr int VT_BYTES = D * VT_STRIDE;   // 18432
-constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
-constexpr int LDS_BYTES = 2 * BUF_BYTES;  // double buffer: 71680
-constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a block
+constexpr int V_BYTES = NKEY * V_STRIDE;  // 20480
+constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+constexpr int LDS_BYTES = 2 * BUF_BYTES;  // double buffer: 75776 (two workgroups per CU)
+constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
+// The reference max of a row moves only when a new score exceeds it by more
+// than 2^8: weights stay <= 256, exact in fp32 and as bf16 operands.
+constexpr float RESCALE_SLACK = 8.0f;
 
-// Position, inside a V^T row of 64 keys, of the group of 4 consecutive keys
-// starting at key 4*g4.  PV consumes keys in k-steps of 16; within k-step kk,
-// lane half h needs keys {16kk+4h+0..3, 16kk+8+4h+0..3} (the keys its S^T
-// registers hold), stored here as 8 contiguous bf16 at 16kk + 8h.
-__device__ __forceinline__ int vt_pos(int g4) {
-  const int kk = g4 >> 2, a = (g4 >> 1) & 1, h = g4 & 1;
-  return 16 * kk + 8 * h + 4 * a;
+typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max / sum of x over the lane pair (l, l ^ 32) that shares one query row
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ shortx4 lds_read_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(const_cast<char *>(p)));
 }
 
 struct MfmaState {
-  float m;          // running max of scaled logits (log2 units)
+  float m;          // reference max of scaled logits (log2 units)
   float lsum;       // this lane's partial sum of 2^(x - m)
   floatx16 acc[4];  // O^T accumulator: 4 blocks of 32 head-dim rows
 };
 
-// One online-softmax step over a 32-entry score block s (already masked with
-// -inf).  Returns the bf16 B operands for PV in pb[0..1].
-__device__ __forceinline__ void softmax_block(MfmaState &st, const floatx16 &s, float scale_log2,
-                                              bf16x8 *pb) {
-  float mx = s[0];
+// Online-softmax update for NB score blocks of 32 entries each (already
+// masked with -inf): move the reference max if needed, turn scores into
+// weights and return them as bf16 B operands, pb[2*i + {0,1}] for block i.
+template <int NB>
+__device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s, float scale_log2,
+                                               bf16x8 *pb) {
+  float mx = s[0][0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, wave_swap32(mx));
-  const float m_new = fmaxf(st.m, mx * scale_log2);
-  const float alpha = fast_exp2(st.m - m_new);
-  st.m = m_new;
-  st.lsum *= alpha;
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+  const float mt = pair_max(mx) * scale_log2;
+  // The branch is wave-wide, but each row moves its reference only when its
+  // own scores ask for it (alpha is exactly 1 otherwise), so a row's result
+  // never depends on the other rows of the wave.
+  const bool need = mt > st.m + RESCALE_SLACK;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_new = need ? mt : st.m;
+    const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
+    st.m = m_new;
+    st.lsum *= alpha;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+  }
+  const float neg_m = -st.m;
   float sum = 0.f;
-  u32x4 w[2];
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const float p0 = fast_exp2(fmaf(s[r], scale_log2, -m_new));
-    const float p1 = fast_exp2(fmaf(s[r + 1], scale_log2, -m_new));
-    sum += p0 + p1;
-    w[r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+  for (int b = 0; b < NB; ++b) {
+    u32x4 w[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(s[b][r], scale_log2, neg_m));
+      const float p1 = fast_exp2(fmaf(s[b][r + 1], scale_log2, neg_m));
+      sum += p0 + p1;
+      w[r >> 3][(r & 7) >> 1] = cvt_bf16x2(p0, p1);
+    }
+    pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
+    pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
   }
   st.lsum += sum;
-  pb[0] = __builtin_bit_cast(bf16x8, w[0]);
-  pb[1] = __builtin_bit_cast(bf16x8, w[1]);
 }
 
 template <bool HAS_DEPTH>
@@ -136,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
   const int64_t ntiles = (T + TQ - 1) / TQ;
-  // Heaviest causal tiles first: block 0..BH-1 take the last tile of each head.
+  // Heaviest causal tiles first: blocks 0..BH-1 take the last tile of each head.
   const int64_t x = blockIdx.x;
   const int64_t tile = ntiles - 1 - x / BH;
   const int64_t bh = x % BH;
@@ -174,26 +207,33 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
   const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
   const int64_t wave_tok_lo = t0 + (wave * 32) / G;
-  const __bf16 *kbase = (const __bf16 *)p.k + bh * T * D;
-  const __bf16 *vbase = (const __bf16 *)p.v + bh * T * D;
-
-  // staging roles: K as 1024 16-byte chunks (4 per thread); V as a 4-key by
-  // 8-dim block per thread, transposed into V^T on the way into LDS.
-  const int v_g4 = tid & 15, v_dg = tid >> 4;
+  // staging: 4 x 16 B of K and of V per thread per tile; row = tid/16 + 16i
+  const char *kg = (const char *)p.k + (bh * T + tid / 16) * (D * 2) + (tid & 15) * 16;
+  const char *vg = (const char *)p.v + (bh * T + tid / 16) * (D * 2) + (tid & 15) * 16;
+  const int k_st = (tid / 16) * K_STRIDE + (tid & 15) * 16;
+  const int v_st = (tid / 16) * V_STRIDE + (tid & 15) * 16;
+  // MFMA operand reads: K rows li (+32), dims 64*lh + 8*ks; V^T through transpose reads
+  const int k_rd = li * K_STRIDE + lh * 128;
+  const int lg = lane >> 4, lq = lane & 15;
+  const int v_rd = (4 * (lg >> 1) + (lq >> 2)) * V_STRIDE + (16 * (lg & 1) + 4 * (lq & 3)) * 2;
   u32x4 kreg[4], vreg[4];
 
   auto gload = [&](int kt) {
-    const int64_t key0 = (int64_t)kt * NKEY;
+    const int64_t off = (int64_t)kt * NKEY * (D * 2);
+    if ((int64_t)(kt + 1) * NKEY <= T) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int64_t key = key0 + (c >> 4);
-      kreg[i] = key < T ? *(const u32x4 *)(kbase + key * D + (c & 15) * 8) : u32x4{0, 0, 0, 0};
-    }
+      for (int i = 0; i < 4; ++i) {
+        kreg[i] = *(const u32x4 *)(kg + off + i * 16 * (D * 2));
+        vreg[i] = *(const u32x4 *)(vg + off + i * 16 * (D * 2));
+      }
+    } else {
+      const int64_t row0 = (int64_t)kt * NKEY + tid / 16;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t key = key0 + 4 * v_g4 + c;
-      vreg[c] = key < T ? *(const u32x4 *)(vbase + key * D + 8 * v_dg) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) {
+        const bool in = row0 + 16 * i < T;
+        kreg[i] = in ? *(const u32x4 *)(kg + off + i * 16 * (D * 2)) : u32x4{0, 0, 0, 0};
+        vreg[i] = in ? *(const u32x4 *)(vg + off + i * 16 * (D * 2)) : u32x4{0, 0, 0, 0};
+      }
     }
   };
   auto lds_store = [&](int buf) {
@@ -201,23 +241,8 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     char *vb = kb + K_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4 *)(kb + (c >> 4) * K_STRIDE + (c & 15) * 16) = kreg[i];
-    }
-    const int pos = vt_pos(v_g4);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int w = n >> 1;
-      uint32_t k0 = vreg[0][w], k1 = vreg[1][w], k2 = vreg[2][w], k3 = vreg[3][w];
-      u32x2 out;
-      if (n & 1) {
-        out[0] = (k0 >> 16) | (k1 & 0xFFFF0000u);
-        out[1] = (k2 >> 16) | (k3 & 0xFFFF0000u);
-      } else {
-        out[0] = (k0 & 0xFFFFu) | (k1 << 16);
-        out[1] = (k2 & 0xFFFFu) | (k3 << 16);
-      }
-      *(u32x2 *)(vb + (8 * v_dg + n) * VT_STRIDE + pos * 2) = out;
+      *(u32x4 *)(kb + k_st + i * 16 * K_STRIDE) = kreg[i];
+      *(u32x4 *)(vb + v_st + i * 16 * V_STRIDE) = vreg[i];
     }
   };
 
@@ -238,56 +263,33 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
       for (int rr = 0; rr < 16; ++rr) s[kb2][rr] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *(const bf16x8 *)(kb + (kb2 * 32 + li) * K_STRIDE + (64 * lh + 8 * ks) * 2);
+        const bf16x8 a = *(const bf16x8 *)(kb + k_rd + kb2 * 32 * K_STRIDE + ks * 16);
         s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kb2], 0, 0, 0);
       }
     }
     const int64_t key0 = (int64_t)kt * NKEY;
     if (key0 + NKEY - 1 > wave_tok_lo) {  // a key past some row's token: causal mask
+      // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
+      int64_t lim64 = tok - key0 - 4 * lh;
+      const int lim = (int)(lim64 < -8 ? -8 : (lim64 > 64 ? 64 : lim64));
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int64_t key = key0 + kb2 * 32 + 8 * (rr >> 2) + 4 * lh + (rr & 3);
-          if (key > tok) s[kb2][rr] = -INFINITY;
-        }
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
     }
-    // one online-softmax update over the whole 64-key tile
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb2][rr]);
-    mx = fmaxf(mx, wave_swap32(mx));
-    const float m_new = fmaxf(st.m, mx * p.scale_log2);
-    const float alpha = fast_exp2(st.m - m_new);
-    st.m = m_new;
-    st.lsum *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] *= alpha;
     bf16x8 pb[4];
-    float sum = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      u32x4 w[2];
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        const float p0 = fast_exp2(fmaf(s[kb2][rr], p.scale_log2, -m_new));
-        const float p1 = fast_exp2(fmaf(s[kb2][rr + 1], p.scale_log2, -m_new));
-        sum += p0 + p1;
-        w[rr >> 3][(rr & 7) >> 1] = pack_bf16x2(p0, p1);
-      }
-      pb[2 * kb2] = __builtin_bit_cast(bf16x8, w[0]);
-      pb[2 * kb2 + 1] = __builtin_bit_cast(bf16x8, w[1]);
-    }
-    st.lsum += sum;
+    softmax_update<2>(st, s, p.scale_log2, pb);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = *(const bf16x8 *)(vb + (32 * nb + li) * VT_STRIDE + (16 * kk + 8 * lh) * 2);
+        const char *vp = vb + v_rd + (16 * kk) * V_STRIDE + nb * 64;
+        const shortx4 lo = lds_read_tr(vp);
+        const shortx4 hi = lds_read_tr(vp + 8 * V_STRIDE);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
         st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], st.acc[nb], 0, 0, 0);
       }
 
@@ -305,41 +307,51 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     if (L > 0 && wt_lo < wt_hi) {
       const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
       const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
-      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes;
+      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
       const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
+      u32x4 kd[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kd[ks] = *(const u32x4 *)(pk + blk_lo * kPackedBlockBytes + ks * 1024);
       for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
         const char *kp = pk + blk * kPackedBlockBytes;
-        const char *vp = kp + BLK_HALF;
-        floatx16 sd;
+        u32x4 vd[8];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sd[rr] = 0.f;
+        for (int j = 0; j < 8; ++j) vd[j] = *(const u32x4 *)(kp + BLK_HALF + j * 1024);
+        floatx16 sd[1];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kp + (ks * 64 + lane) * 16));
-          sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sd, 0, 0, 0);
+        for (int rr = 0; rr < 16; ++rr) sd[0][rr] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          sd[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]),
+                                                          qb[ks], sd[0], 0, 0, 0);
+        if (blk + 1 < blk_hi) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            kd[ks] = *(const u32x4 *)(kp + kPackedBlockBytes + ks * 1024);
         }
-        const int64_t e0 = blk * kDepthBlock;
+        // entry of register rr: blk*32 + 8*(rr/4) + 4*lh + rr%4; keep it iff it
+        // belongs to this row's token
+        // (clamped to [-64, L]: every clamped value keeps the keep/drop decision)
+        int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
+        const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int64_t e = e0 + 8 * (rr >> 2) + 4 * lh + (rr & 3);
-          if ((uint64_t)(e - my_lo) >= (uint64_t)L) sd[rr] = -INFINITY;
-        }
+        for (int rr = 0; rr < 16; ++rr)
+          if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[0][rr] = -INFINITY;
         bf16x8 pb[2];
-        softmax_block(st, sd, p.scale_log2, pb);
+        softmax_update<1>(st, sd, p.scale_log2, pb);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 a =
-                __builtin_bit_cast(bf16x8, *(const u32x4 *)(vp + ((nb * 2 + kk) * 64 + lane) * 16));
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], st.acc[nb], 0, 0, 0);
-          }
+          for (int kk = 0; kk < 2; ++kk)
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, vd[nb * 2 + kk]), pb[kk], st.acc[nb], 0, 0, 0);
       }
     }
   }
 
   // ---------------- epilogue: the single normalisation
-  const float ltot = st.lsum + wave_swap32(st.lsum);
+  const float ltot = pair_sum(st.lsum);
   if (row_ok) {
     const float inv = 1.0f / ltot;
     __bf16 *orow = (__bf16 *)p.out + ((b * p.Hq + head) * T + tok) * D;
@@ -348,8 +360,8 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 o;
-        o[0] = pack_bf16x2(st.acc[nb][4 * g + 0] * inv, st.acc[nb][4 * g + 1] * inv);
-        o[1] = pack_bf16x2(st.acc[nb][4 * g + 2] * inv, st.acc[nb][4 * g + 3] * inv);
+        o[0] = cvt_bf16x2(st.acc[nb][4 * g + 0] * inv, st.acc[nb][4 * g + 1] * inv);
+        o[1] = cvt_bf16x2(st.acc[nb][4 * g + 2] * inv, st.acc[nb][4 * g + 3] * inv);
         *(u32x2 *)(orow + 32 * nb + 8 * g + 4 * lh) = o;
       }
     if (p.lse && lh == 0)

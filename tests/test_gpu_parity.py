@@ -70,7 +70,8 @@ MFMA_SHAPES = [
     (1, 2, 1, 1, 0), (1, 2, 1, 1, 3), (1, 4, 1, 17, 1), (1, 4, 2, 129, 3),
     (2, 8, 2, 1000, 24), (1, 16, 4, 200, 0), (1, 3, 1, 50, 5), (1, 4, 4, 77, 2),
     (1, 32, 2, 130, 4), (1, 64, 2, 40, 3), (1, 24, 1, 33, 2), (1, 8, 1, 300, 40),
-    (1, 16, 4, 64, 32), (2, 4, 1, 65, 7),
+    (1, 16, 4, 64, 32), (2, 4, 1, 65, 7), (1, 16, 4, 70, 100), (1, 4, 4, 9, 129),
+    (1, 8, 1, 40, 65),
 ]
 
 
