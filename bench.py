@@ -180,6 +180,29 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True):
     return res
 
 
+def profile_only(cfg, which, steps):
+    """Launch one kernel `steps` times on the workload (for rocprofv3 --pmc)."""
+    import torch
+    from depth_wise_kv_amd import moda
+    from synth import torch_inputs
+    dev = torch.device("cuda:0")
+    d_in = torch_inputs(cfg, dev)
+    L = cfg["L"]
+    shape = moda.make_shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], L, cfg["d"], cfg["dtype"])
+    packed = moda.pack_depth_cache(d_in["kd"], d_in["vd"], shape) if L else None
+    out = torch.empty_like(d_in["q"])
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        if which == "fwd":
+            moda.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, out=out)
+        elif which == "causal":
+            moda.causal_fwd(d_in["q"], d_in["k"], d_in["v"], out=out)
+        else:
+            moda.pack_depth_cache(d_in["kd"], d_in["vd"], shape, out=packed)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": which, "workload": cfg, "launches": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +211,10 @@ def main():
     ap.add_argument("--config", default="long_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack"],
+                    help="only launch this kernel (steps times) for counter collection")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy a 1 GiB buffer (steps times): HBM counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -195,6 +222,20 @@ def main():
         sys.exit(2)
 
     from synth import WORKLOADS, sweep_points
+
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
+    if args.profile_kernel:
+        profile_only(dict(WORKLOADS[args.config]), args.profile_kernel, args.steps)
+        return
 
     if args.sweep:
         for c in sweep_points():
