@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moda_internal.h"
 
 namespace moda {
@@ -105,6 +107,39 @@ __device__ __forceinline__ shortx4 lds_read_tr(const char *p) {
       (__attribute__((address_space(3))) shortx4 *)(const_cast<char *>(p)));
 }
 
+// Optional cycle tracing of the fused kernel's phases (off unless the build
+// defines MODA_TRACE_ENABLED; then moda_trace_buf receives per-phase cycle
+// sums, summed over waves, from the shader clock).
+#ifdef MODA_TRACE_ENABLED
+__device__ unsigned long long moda_trace_buf[16];
+#define MODA_TRACE_DECL                          \
+  long long tr_last = __builtin_amdgcn_s_memtime(); \
+  long long tr_acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#define MODA_TRACE(i)                                   \
+  do {                                                  \
+    const long long tr_now = __builtin_amdgcn_s_memtime(); \
+    tr_acc[i] += tr_now - tr_last;                      \
+    tr_last = tr_now;                                   \
+  } while (0)
+#define MODA_TRACE_FLUSH                                                            \
+  do {                                                                              \
+    if ((threadIdx.x & 63) == 0)                                                    \
+      for (int i_ = 0; i_ < 8; ++i_) atomicAdd(&moda_trace_buf[i_], (unsigned long long)tr_acc[i_]); \
+  } while (0)
+#else
+#define MODA_TRACE_DECL
+#define MODA_TRACE(i) \
+  do {                \
+  } while (0)
+#define MODA_TRACE_FLUSH \
+  do {                   \
+  } while (0)
+#endif
+
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
+
 struct MfmaState {
   float m;          // reference max of scaled logits (log2 units)
   float lsum;       // this lane's partial sum of 2^(x - m)
@@ -155,15 +190,43 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
   st.lsum += sum;
 }
 
+// ---------------------------------------------------------------------------
+// Fused forward, MFMA path.
+//
+// A workgroup has 4 waves and owns 128 query rows (32 per wave); two
+// workgroups share a CU, so every SIMD runs two waves.  K and V tiles of 64
+// keys go straight from global memory into LDS (buffer_load_dwordx4 ... lds), no
+// registers in between, into XOR-swizzled 16 KiB buffers:
+//   K: 16-byte chunk c of key row r sits in slot c ^ (r % 16)    (ds_read_b128
+//      of 16 consecutive rows at one chunk hits 16 distinct slots)
+//   V: chunk c of key row r sits in slot c ^ 4*(r % 4)           (each 16-lane
+//      group of a transpose read touches 4 rows x 2 chunks, 8 distinct slots)
+// The key loop is software-pipelined inside each wave: iteration j issues the
+// loads of K(j+2) and V(j+1), computes S(j+1) = K(j+1) Q^T on the matrix cores
+// while the VALU turns S(j) into weights, then runs PV(j) while the VALU
+// reduces S(j+1) to its row maxima.  Iteration j reads K buffer (j+1)%2 and V
+// buffer j%2 and fills K buffer j%2 and V buffer (j+1)%2, whose last readers
+// finished before the barrier that ends iteration j-1.  The four buffers are
+// distinct LDS objects and the loop is unrolled by buffer parity, so the
+// compiler can see that the loads in flight never alias the buffers read.
+// ---------------------------------------------------------------------------
+constexpr int TILE_BYTES = NKEY * D * 2;  // 16 KiB: one K or V tile
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 template <bool HAS_DEPTH>
 __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   // A tile holds TQ = floor(128 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lh = lane >> 5;
 
   const int64_t T = p.T;
@@ -202,99 +265,159 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] = 0.f;
+  const float sc = p.scale_log2;
 
-  // ---------------- sequence part: key tiles 0 .. the tile's last token
+  // ---------------- sequence part
   const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
   const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
   const int64_t wave_tok_lo = t0 + (wave * 32) / G;
-  // staging: 4 x 16 B of K and of V per thread per tile; row = tid/16 + 16i
-  const char *kg = (const char *)p.k + (bh * T + tid / 16) * (D * 2) + (tid & 15) * 16;
-  const char *vg = (const char *)p.v + (bh * T + tid / 16) * (D * 2) + (tid & 15) * 16;
-  const int k_st = (tid / 16) * K_STRIDE + (tid & 15) * 16;
-  const int v_st = (tid / 16) * V_STRIDE + (tid & 15) * 16;
-  // MFMA operand reads: K rows li (+32), dims 64*lh + 8*ks; V^T through transpose reads
-  const int k_rd = li * K_STRIDE + lh * 128;
-  const int lg = lane >> 4, lq = lane & 15;
-  const int v_rd = (4 * (lg >> 1) + (lq >> 2)) * V_STRIDE + (16 * (lg & 1) + 4 * (lq & 3)) * 2;
-  u32x4 kreg[4], vreg[4];
 
-  auto gload = [&](int kt) {
-    const int64_t off = (int64_t)kt * NKEY * (D * 2);
+  // direct loads: instruction i of this wave fills tile rows 16*wave + 4i .. +3.
+  // Buffer descriptors cover one (b, kv head) of K and of V; the tile offset
+  // goes in the scalar offset, the lane's row/chunk in the vector offset.
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.k + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.v + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
+  const int dma_row = 16 * wave + (lane >> 4);  // + 4i
+  uint32_t dk_off[4], dv_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = dma_row + 4 * i;
+    dk_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (row & 15)));
+    dv_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3))));
+  }
+  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, char *lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
+                                             16, voff, soff, 0, 0);
+  };
+  // tile kt of K and V into the given buffers
+  auto dma_tiles = [&](int kt, char *k_dst, char *v_dst) {
+    k_dst += wave * 4096;
+    v_dst += wave * 4096;
     if ((int64_t)(kt + 1) * NKEY <= T) {
+      const uint32_t soff = (uint32_t)kt * TILE_BYTES;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kreg[i] = *(const u32x4 *)(kg + off + i * 16 * (D * 2));
-        vreg[i] = *(const u32x4 *)(vg + off + i * 16 * (D * 2));
+        dma(k_rsrc, k_dst + i * 1024, dk_off[i], soff);
+        dma(v_rsrc, v_dst + i * 1024, dv_off[i], soff);
       }
-    } else {
-      const int64_t row0 = (int64_t)kt * NKEY + tid / 16;
+    } else {  // past the end: row T-1, finite data that every mask removes
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool in = row0 + 16 * i < T;
-        kreg[i] = in ? *(const u32x4 *)(kg + off + i * 16 * (D * 2)) : u32x4{0, 0, 0, 0};
-        vreg[i] = in ? *(const u32x4 *)(vg + off + i * 16 * (D * 2)) : u32x4{0, 0, 0, 0};
+        const int trow = dma_row + 4 * i;
+        int64_t row = (int64_t)kt * NKEY + trow;
+        row = row < T ? row : T - 1;
+        const uint32_t rbase = (uint32_t)row * 256 - (uint32_t)trow * 256;
+        dma(k_rsrc, k_dst + i * 1024, dk_off[i] + rbase, 0);
+        dma(v_rsrc, v_dst + i * 1024, dv_off[i] + rbase, 0);
       }
     }
   };
-  auto lds_store = [&](int buf) {
-    char *kb = smem + buf * BUF_BYTES;
-    char *vb = kb + K_BYTES;
+  // MFMA operand reads.  K: row 32*kb2 + li, chunk 8*lh + ks, in slot
+  // (8*lh + ks) ^ (li % 16) = (8*lh ^ (li & 8)) + (ks ^ (li & 7)).
+  const int k_row = li * 256 + 16 * ((8 * lh) ^ (li & 8));
+  const int k_x = li & 7;
+  // V (transpose reads): lane group lg = lane/16 and lq = lane%16 read key row
+  // 16*kk + 8*hi + 4*(lg/2) + lq/4, dims 32*nb + 16*(lg%2) + 4*(lq%4) .. +3.
+  const int lg = lane >> 4, lq = lane & 15;
+  int vaddr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4 *)(kb + k_st + i * 16 * K_STRIDE) = kreg[i];
-      *(u32x4 *)(vb + v_st + i * 16 * V_STRIDE) = vreg[i];
-    }
+  for (int nb = 0; nb < 4; ++nb)
+    vaddr[nb] = (4 * (lg >> 1) + (lq >> 2)) * 256 +
+                16 * (4 * (nb ^ (lq >> 2)) + 2 * (lg & 1) + ((lq & 3) >> 1)) + 8 * (lq & 1);
+
+  auto kfrag = [&](const char *kb, int i) {  // i = 2*ks + kb2
+    return *(const bf16x8 *)(kb + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
+  };
+  auto vfrag = [&](const char *vb, int i) {  // i = 4*nb + kk
+    const char *vp = vb + vaddr[i >> 2] + 16 * (i & 3) * 256;
+    const shortx4 lo = lds_read_tr(vp);
+    const shortx4 hi = lds_read_tr(vp + 8 * 256);
+    return __builtin_bit_cast(
+        bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+  };
+  auto mask = [&](floatx16 (&s)[2], int kt) {
+    // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
+    const int lim = (int)max((int64_t)-8, min((int64_t)64, tok - (int64_t)kt * NKEY - 4 * lh));
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
   };
 
-  gload(0);
-  lds_store(0);
+  MODA_TRACE_DECL
+  dma_tiles(0, k_lds0, v_lds0);
+  wait_vmem();
   __syncthreads();
+  MODA_TRACE(0);  // prologue
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) gload(kt + 1);
-    const char *kb = smem + buf * BUF_BYTES;
-    const char *vb = kb + K_BYTES;
-
+  // iteration j with buffer parity P = j % 2: loads tile j+1 into the other
+  // buffers (last read in iteration j-1), computes tile j
+  auto body = [&](int j, auto parity, auto masked) {
+    constexpr int P = decltype(parity)::value;
+    const char *const k_rd = P ? k_lds1 : k_lds0;
+    const char *const v_rd = P ? v_lds1 : v_lds0;
+    if (j + 1 < n_kt) dma_tiles(j + 1, P ? k_lds0 : k_lds1, P ? v_lds0 : v_lds1);
+    MODA_TRACE(1);  // load issue
+    // S^T = K Q^T: the two 32-key chains alternate; reads run four ahead
     floatx16 s[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[kb2][rr] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = *(const bf16x8 *)(kb + k_rd + kb2 * 32 * K_STRIDE + ks * 16);
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kb2], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int ks = i >> 1, kb2 = i & 1;
+      const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
+      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(k_rd, i), qb[ks], c, 0, 0, 0);
     }
-    const int64_t key0 = (int64_t)kt * NKEY;
-    if (key0 + NKEY - 1 > wave_tok_lo) {  // a key past some row's token: causal mask
-      // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
-      int64_t lim64 = tok - key0 - 4 * lh;
-      const int lim = (int)(lim64 < -8 ? -8 : (lim64 > 64 ? 64 : lim64));
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+    MODA_TRACE(2);  // QK^T
+    if constexpr (decltype(masked)::value) mask(s, j);
     bf16x8 pb[4];
-    softmax_update<2>(st, s, p.scale_log2, pb);
+    softmax_update<2>(st, s, sc, pb);
+    MODA_TRACE(3);  // mask + softmax
+    // O^T += V^T P^T: three fragments (six transpose reads) ahead
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int i = 0; i < 16; ++i)
+      st.acc[i >> 2] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(v_rd, i), pb[i & 3], st.acc[i >> 2], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char *vp = vb + v_rd + (16 * kk) * V_STRIDE + nb * 64;
-        const shortx4 lo = lds_read_tr(vp);
-        const shortx4 hi = lds_read_tr(vp + 8 * V_STRIDE);
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                            __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], st.acc[nb], 0, 0, 0);
-      }
-
-    if (kt + 1 < n_kt) lds_store(buf ^ 1);
+    for (int i = 0; i < 13; ++i) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 1);
+    MODA_TRACE(4);  // PV
+    wait_vmem();
+    MODA_TRACE(5);  // wait for this wave's loads
     __syncthreads();
+    MODA_TRACE(6);  // barrier
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // key tiles [0, n_nm) lie entirely at or before this wave's first token
+  const int n_nm = (int)min((int64_t)n_kt, (wave_tok_lo + 1) / NKEY);
+  int j = 0;
+  for (; j + 1 < n_nm; j += 2) {
+    body(j, I0{}, std::false_type{});
+    body(j + 1, I1{}, std::false_type{});
+  }
+  for (; j < n_kt; ++j) {
+    const bool mk = j >= n_nm;
+    if (j & 1) {
+      if (mk) body(j, I1{}, std::true_type{});
+      else body(j, I1{}, std::false_type{});
+    } else {
+      if (mk) body(j, I0{}, std::true_type{});
+      else body(j, I0{}, std::false_type{});
+    }
   }
 
   // ---------------- depth part: this wave's tokens' contiguous depth span
@@ -350,6 +473,8 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     }
   }
 
+  MODA_TRACE(7);  // depth part
+  MODA_TRACE_FLUSH;
   // ---------------- epilogue: the single normalisation
   const float ltot = pair_sum(st.lsum);
   if (row_ok) {

@@ -14,7 +14,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoda.so")
+# MODA_LIBRARY may point at another build of the same library (e.g. an
+# instrumented one); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MODA_LIBRARY") or os.path.join(_HERE, "libmoda.so")
 
 MODA_OK, MODA_ERR_INVALID_ARG, MODA_ERR_UNSUPPORTED, MODA_ERR_HIP = 0, 1, 2, 3
 MODA_F32, MODA_BF16 = 0, 1
