@@ -291,28 +291,14 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
                                              16, voff, soff, 0, 0);
   };
-  // tile kt of K and V into the given buffers
-  auto dma_tiles = [&](int kt, char *k_dst, char *v_dst) {
-    k_dst += wave * 4096;
-    v_dst += wave * 4096;
-    if ((int64_t)(kt + 1) * NKEY <= T) {
-      const uint32_t soff = (uint32_t)kt * TILE_BYTES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dma(k_rsrc, k_dst + i * 1024, dk_off[i], soff);
-        dma(v_rsrc, v_dst + i * 1024, dv_off[i], soff);
-      }
-    } else {  // past the end: row T-1, finite data that every mask removes
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int trow = dma_row + 4 * i;
-        int64_t row = (int64_t)kt * NKEY + trow;
-        row = row < T ? row : T - 1;
-        const uint32_t rbase = (uint32_t)row * 256 - (uint32_t)trow * 256;
-        dma(k_rsrc, k_dst + i * 1024, dk_off[i] + rbase, 0);
-        dma(v_rsrc, v_dst + i * 1024, dv_off[i] + rbase, 0);
-      }
-    }
+  // instruction q (0..7) of the loads of tile kt: q < 4 loads K rows, q >= 4
+  // V rows.  Rows at or past T fall outside the descriptor's range and read as
+  // zeros, which every mask removes.
+  auto dma_one = [&](int q, int kt, char *k_dst, char *v_dst) {
+    const uint32_t soff = (uint32_t)kt * TILE_BYTES;
+    const int i = q & 3;
+    if (q < 4) dma(k_rsrc, k_dst + wave * 4096 + i * 1024, dk_off[i], soff);
+    else dma(v_rsrc, v_dst + wave * 4096 + i * 1024, dv_off[i], soff);
   };
   // MFMA operand reads.  K: row 32*kb2 + li, chunk 8*lh + ks, in slot
   // (8*lh + ks) ^ (li % 16) = (8*lh ^ (li & 8)) + (ks ^ (li & 7)).
@@ -349,7 +335,16 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   };
 
   MODA_TRACE_DECL
-  dma_tiles(0, k_lds0, v_lds0);
+  // start from zeroed buffers: loads of rows past T may leave LDS untouched
+  for (int o = tid * 16; o < TILE_BYTES; o += 256 * 16) {
+    *(u32x4 *)(k_lds0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(k_lds1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(v_lds0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(v_lds1 + o) = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma_one(q, 0, k_lds0, v_lds0);
   wait_vmem();
   __syncthreads();
   MODA_TRACE(0);  // prologue
@@ -360,40 +355,47 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     constexpr int P = decltype(parity)::value;
     const char *const k_rd = P ? k_lds1 : k_lds0;
     const char *const v_rd = P ? v_lds1 : v_lds0;
-    if (j + 1 < n_kt) dma_tiles(j + 1, P ? k_lds0 : k_lds1, P ? v_lds0 : v_lds1);
-    MODA_TRACE(1);  // load issue
-    // S^T = K Q^T: the two 32-key chains alternate; reads run four ahead
+    char *const k_wr = P ? k_lds0 : k_lds1;
+    char *const v_wr = P ? v_lds0 : v_lds1;
+    MODA_TRACE(1);  // (loads are issued inside the QK^T sequence)
+    // S^T = K Q^T: the two 32-key chains alternate, K fragments are read four
+    // MFMAs ahead and the eight loads of tile j+1 are spread between the
+    // MFMAs; sched_barrier fences keep this order.
     floatx16 s[2];
+    {
+      bf16x8 a[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ks = i >> 1, kb2 = i & 1;
-      const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
-      s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(k_rd, i), qb[ks], c, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+      for (int i = 0; i < 4; ++i) a[i] = kfrag(k_rd, i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int ks = i >> 1, kb2 = i & 1;
+        const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], qb[ks], c, 0, 0, 0);
+        if (i + 4 < 16) a[i & 3] = kfrag(k_rd, i + 4);
+        if ((i & 1) == 0) dma_one(i >> 1, j + 1, k_wr, v_wr);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
     MODA_TRACE(2);  // QK^T
     if constexpr (decltype(masked)::value) mask(s, j);
     bf16x8 pb[4];
     softmax_update<2>(st, s, sc, pb);
     MODA_TRACE(3);  // mask + softmax
-    // O^T += V^T P^T: three fragments (six transpose reads) ahead
+    // O^T += V^T P^T: V fragments (two transpose reads each) three MFMAs ahead
+    {
+      bf16x8 a[3];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      st.acc[i >> 2] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(v_rd, i), pb[i & 3], st.acc[i >> 2], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 1);
+      for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 13; ++i) {
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
+      for (int i = 0; i < 16; ++i) {
+        st.acc[i >> 2] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[i & 3], st.acc[i >> 2], 0, 0, 0);
+        if (i + 3 < 16) a[i % 3] = vfrag(v_rd, i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 1);
     MODA_TRACE(4);  // PV
     wait_vmem();
     MODA_TRACE(5);  // wait for this wave's loads
