@@ -50,14 +50,14 @@ moda_status check_shape_impl(const moda_shape *s) {
     return fail(MODA_ERR_INVALID_ARG, "dtype must be MODA_F32 or MODA_BF16");
   if (s->d != 32 && s->d != 64 && s->d != 128)
     return fail(MODA_ERR_UNSUPPORTED, "head dim d must be 32, 64 or 128");
-  if (s->dtype == MODA_BF16 && s->d == moda::kMfmaD && s->T > ((int64_t)1 << 23))
-    return fail(MODA_ERR_UNSUPPORTED, "bf16 with d = 128 supports T up to 2^23");
-  if (s->dtype == MODA_BF16 && s->d == moda::kMfmaD && s->Hq / s->Hkv > moda::kMfmaRows)
-    return fail(MODA_ERR_UNSUPPORTED, "bf16 with d = 128 supports G = Hq / Hkv up to 128");
   if (checked_prod({s->B, s->Hq, s->T, s->d}) < 0 ||
       checked_prod({s->B, s->Hkv, s->T, s->L, s->d}) < 0 ||
       checked_prod({s->B, s->Hkv, s->T, s->L, s->d, 4}) < 0)
     return fail(MODA_ERR_INVALID_ARG, "tensor size overflows");
+  if (s->dtype == MODA_BF16 && s->d == moda::kMfmaD && s->T > ((int64_t)1 << 23))
+    return fail(MODA_ERR_UNSUPPORTED, "bf16 with d = 128 supports T up to 2^23");
+  if (s->dtype == MODA_BF16 && s->d == moda::kMfmaD && s->Hq / s->Hkv > moda::kMfmaRows)
+    return fail(MODA_ERR_UNSUPPORTED, "bf16 with d = 128 supports G = Hq / Hkv up to 256");
   return MODA_OK;
 }
 

@@ -9,7 +9,7 @@ namespace moda {
 
 // Geometry of the MFMA path (bf16, head dim 128).
 constexpr int kMfmaD = 128;         // head dimension
-constexpr int kMfmaRows = 128;      // query rows (token x head pairs) per workgroup
+constexpr int kMfmaRows = 256;      // query rows (token x head pairs) per workgroup
 constexpr int kDepthBlock = 32;     // depth entries per packed block
 constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part + V part
 

@@ -71,12 +71,6 @@ __device__ __forceinline__ float wave_swap32(float x) {
 constexpr int D = kMfmaD;             // 128
 constexpr int M = kMfmaRows;          // 128 query rows per workgroup
 constexpr int NKEY = 64;              // keys per sequence tile
-constexpr int K_STRIDE = D * 2 + 16;  // bytes per K row in LDS: conflict-free ds_read_b128
-constexpr int V_STRIDE = D * 2 + 64;  // bytes per V row in LDS: conflict-free transpose reads
-constexpr int K_BYTES = NKEY * K_STRIDE;  // 17408
-constexpr int V_BYTES = NKEY * V_STRIDE;  // 20480
-constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-constexpr int LDS_BYTES = 2 * BUF_BYTES;  // double buffer: 75776 (two workgroups per CU)
 constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
 // The reference max of a row moves only when a new score exceeds it by more
 // than 2^8: weights stay <= 256, exact in fp32 and as bf16 operands.
@@ -193,8 +187,8 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
 // ---------------------------------------------------------------------------
 // Fused forward, MFMA path.
 //
-// A workgroup has 4 waves and owns 128 query rows (32 per wave); two
-// workgroups share a CU, so every SIMD runs two waves.  K and V tiles of 64
+// A workgroup has 8 waves and owns 256 query rows (32 per wave): two waves on
+// every SIMD, and each K/V tile brought into LDS serves 256 rows.  K and V tiles of 64
 // keys go straight from global memory into LDS (buffer_load_dwordx4 ... lds), no
 // registers in between, into XOR-swizzled 16 KiB buffers:
 //   K: 16-byte chunk c of key row r sits in slot c ^ (r % 16)    (ds_read_b128
@@ -211,11 +205,15 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
 // compiler can see that the loads in flight never alias the buffers read.
 // ---------------------------------------------------------------------------
 constexpr int TILE_BYTES = NKEY * D * 2;  // 16 KiB: one K or V tile
+constexpr int NWAVE = M / 32;             // waves per workgroup, 32 query rows each
+constexpr int DMA_ROWS = NKEY / NWAVE;    // tile rows each wave loads
+constexpr int DMA_INSTR = DMA_ROWS / 4;   // 1 KiB (4-row) load instructions per wave per tile
+static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divide the MFMAs");
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <bool HAS_DEPTH>
-__global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
+__global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   // A tile holds TQ = floor(128 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
@@ -279,10 +277,10 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
       (void *)((const char *)p.k + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.v + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
-  const int dma_row = 16 * wave + (lane >> 4);  // + 4i
-  uint32_t dk_off[4], dv_off[4];
+  const int dma_row = DMA_ROWS * wave + (lane >> 4);  // + 4i
+  uint32_t dk_off[DMA_INSTR], dv_off[DMA_INSTR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < DMA_INSTR; ++i) {
     const int row = dma_row + 4 * i;
     dk_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (row & 15)));
     dv_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3))));
@@ -291,14 +289,14 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
                                              16, voff, soff, 0, 0);
   };
-  // instruction q (0..7) of the loads of tile kt: q < 4 loads K rows, q >= 4
-  // V rows.  Rows at or past T fall outside the descriptor's range and read as
+  // instruction q of this wave's 2*DMA_INSTR loads of tile kt: q < DMA_INSTR
+  // loads K rows, the rest V rows.  Rows at or past T fall outside the descriptor's range and read as
   // zeros, which every mask removes.
   auto dma_one = [&](int q, int kt, char *k_dst, char *v_dst) {
     const uint32_t soff = (uint32_t)kt * TILE_BYTES;
-    const int i = q & 3;
-    if (q < 4) dma(k_rsrc, k_dst + wave * 4096 + i * 1024, dk_off[i], soff);
-    else dma(v_rsrc, v_dst + wave * 4096 + i * 1024, dv_off[i], soff);
+    const int i = q % DMA_INSTR;
+    if (q < DMA_INSTR) dma(k_rsrc, k_dst + wave * DMA_ROWS * 256 + i * 1024, dk_off[i], soff);
+    else dma(v_rsrc, v_dst + wave * DMA_ROWS * 256 + i * 1024, dv_off[i], soff);
   };
   // MFMA operand reads.  K: row 32*kb2 + li, chunk 8*lh + ks, in slot
   // (8*lh + ks) ^ (li % 16) = (8*lh ^ (li & 8)) + (ks ^ (li & 7)).
@@ -336,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
 
   MODA_TRACE_DECL
   // start from zeroed buffers: loads of rows past T may leave LDS untouched
-  for (int o = tid * 16; o < TILE_BYTES; o += 256 * 16) {
+  for (int o = tid * 16; o < TILE_BYTES; o += 64 * NWAVE * 16) {
     *(u32x4 *)(k_lds0 + o) = u32x4{0, 0, 0, 0};
     *(u32x4 *)(k_lds1 + o) = u32x4{0, 0, 0, 0};
     *(u32x4 *)(v_lds0 + o) = u32x4{0, 0, 0, 0};
@@ -344,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
   }
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_one(q, 0, k_lds0, v_lds0);
+  for (int q = 0; q < 2 * DMA_INSTR; ++q) dma_one(q, 0, k_lds0, v_lds0);
   wait_vmem();
   __syncthreads();
   MODA_TRACE(0);  // prologue
@@ -373,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_mfma(FwdArgs p) {
         const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
         s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], qb[ks], c, 0, 0, 0);
         if (i + 4 < 16) a[i & 3] = kfrag(k_rd, i + 4);
-        if ((i & 1) == 0) dma_one(i >> 1, j + 1, k_wr, v_wr);
+        if (i % (16 / (2 * DMA_INSTR)) == 0) dma_one(i / (16 / (2 * DMA_INSTR)), j + 1, k_wr, v_wr);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -668,9 +666,9 @@ hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const int64_t grid = ntiles * a.B * a.Hkv;
   if (a.has_depth)
-    hipLaunchKernelGGL((moda_fwd_mfma<true>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<true>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s, a);
   else
-    hipLaunchKernelGGL((moda_fwd_mfma<false>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<false>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s, a);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def test_check_shape(m):
     assert m.moda_check_shape(shape(m, T=0)) == m.MODA_ERR_INVALID_ARG
     assert m.moda_check_shape(shape(m, L=-1)) == m.MODA_ERR_INVALID_ARG
     assert m.moda_check_shape(shape(m, d=96)) == m.MODA_ERR_UNSUPPORTED
-    assert m.moda_check_shape(shape(m, Hq=256, Hkv=1)) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_check_shape(shape(m, Hq=512, Hkv=1)) == m.MODA_ERR_UNSUPPORTED
     assert m.moda_check_shape(shape(m, T=1 << 40, L=1 << 20)) == m.MODA_ERR_INVALID_ARG
     s = shape(m)
     s.dtype = 7
