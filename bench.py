@@ -54,6 +54,21 @@ def pack_bytes(c):
     return 2 * (2 * c["B"] * c["Hkv"] * c["T"] * c["L"] * c["d"] * es(c))
 
 
+def roofline(c, fwd_ms, traffic):
+    """Roofline of the fused kernel: matrix-core-bound when its arithmetic
+    intensity (algorithmic flops per algorithmic HBM byte) is above the ridge
+    point of the two published peaks, HBM-bound below it."""
+    ai = flops(c) / fused_bytes(c)
+    if ai >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        a = flops(c) / fwd_ms / 1e9
+        return {"bound": "mfma", "kernel": "moda_fwd_mfma<true>", "achieved": a,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS,
+                "traffic": traffic}
+    a = fused_bytes(c) / fwd_ms / 1e6
+    return {"bound": "hbm", "kernel": "moda_fwd_mfma<true>", "achieved": a,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS, "traffic": traffic}
+
+
 def kernel_src_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -211,6 +226,8 @@ def main():
     ap.add_argument("--config", default="long_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="with --sweep: run only points whose name contains this string")
     ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,17 +245,32 @@ def main():
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(args.steps):
             dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps + 1,
+                          "ms_per_copy": ms, "read_plus_write_gbs": 2 * n / ms / 1e6}),
+              flush=True)
         return
+    named = dict(WORKLOADS)
+    named.update({c["name"]: c for c in sweep_points()})
+    if args.config not in named:
+        print(f"bench.py: unknown config {args.config!r}", file=sys.stderr)
+        sys.exit(2)
     if args.profile_kernel:
-        profile_only(dict(WORKLOADS[args.config]), args.profile_kernel, args.steps)
+        profile_only(dict(named[args.config]), args.profile_kernel, args.steps)
         return
 
     if args.sweep:
         for c in sweep_points():
+            if args.only and args.only not in c["name"]:
+                continue
             r = bench_config(c, args.steps, args.warmup, False, causal=True)
             print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
@@ -249,7 +281,7 @@ def main():
                               "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6}), flush=True)
         return
 
-    cfg = dict(WORKLOADS[args.config])
+    cfg = dict(named[args.config])
     r = bench_config(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
     F = flops(cfg)
     step_ms = r["wall_ms"]
@@ -281,9 +313,8 @@ def main():
         "ratio_fwd_over_causal": r["fwd_ms"] / r["causal_ms"],
         "ratio_step_over_causal": step_ms / r["causal_ms"],
         "pack_hbm_gbs": pack_bytes(cfg) / r["pack_ms"] / 1e6 if r["pack_ms"] else None,
-        "roofline": {"bound": "mfma", "kernel": "moda_fwd_mfma<true>",
-                     "achieved": fwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "fwd_hbm_gbs": fused_bytes(cfg) / r["fwd_ms"] / 1e6,
+        "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:
         line["cpu_baseline"] = r["cpu_baseline"]

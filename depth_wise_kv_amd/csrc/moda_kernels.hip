@@ -9,8 +9,8 @@
 // "Hardware-efficient implementation").
 //
 // Kernels:
-//   moda_fwd_mfma   bf16, d = 128.  A workgroup owns 128 query rows made of
-//                   128/G tokens x the G heads of one KV group, so one K/V
+//   moda_fwd_mfma   bf16, d = 128.  A workgroup owns 256 query rows made of
+//                   256/G tokens x the G heads of one KV group, so one K/V
 //                   tile in LDS and one depth span serve all G heads (the
 //                   group-aware indexing of the same section).  QK^T and PV
 //                   run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "moda_internal.h"
+
 
 namespace moda {
 
@@ -69,7 +70,7 @@ __device__ __forceinline__ float wave_swap32(float x) {
 // sum are in-lane work plus one exchange with lane l ^ 32.
 // ---------------------------------------------------------------------------
 constexpr int D = kMfmaD;             // 128
-constexpr int M = kMfmaRows;          // 128 query rows per workgroup
+constexpr int M = kMfmaRows;          // 256 query rows per workgroup
 constexpr int NKEY = 64;              // keys per sequence tile
 constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
 // The reference max of a row moves only when a new score exceeds it by more
@@ -130,10 +131,6 @@ __device__ unsigned long long moda_trace_buf[16];
   } while (0)
 #endif
 
-// instruction classes for __builtin_amdgcn_sched_group_barrier
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DS_READ = 0x100;
-
 struct MfmaState {
   float m;          // reference max of scaled logits (log2 units)
   float lsum;       // this lane's partial sum of 2^(x - m)
@@ -166,7 +163,8 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
   }
-  const float neg_m = -st.m;
+  // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
+  const float neg_m = st.m == -INFINITY ? 0.f : -st.m;
   float sum = 0.f;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -195,13 +193,12 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
 //      of 16 consecutive rows at one chunk hits 16 distinct slots)
 //   V: chunk c of key row r sits in slot c ^ 4*(r % 4)           (each 16-lane
 //      group of a transpose read touches 4 rows x 2 chunks, 8 distinct slots)
-// The key loop is software-pipelined inside each wave: iteration j issues the
-// loads of K(j+2) and V(j+1), computes S(j+1) = K(j+1) Q^T on the matrix cores
-// while the VALU turns S(j) into weights, then runs PV(j) while the VALU
-// reduces S(j+1) to its row maxima.  Iteration j reads K buffer (j+1)%2 and V
-// buffer j%2 and fills K buffer j%2 and V buffer (j+1)%2, whose last readers
-// finished before the barrier that ends iteration j-1.  The four buffers are
-// distinct LDS objects and the loop is unrolled by buffer parity, so the
+// Iteration j of the key loop computes S(j) = K(j) Q^T, turns it into weights,
+// adds V(j)^T P(j)^T to the accumulator, and meanwhile loads tile j+1 (this
+// wave's eighth of it) into the other K and V buffers, whose last readers
+// finished before the barrier that ended iteration j-1.  The two waves that
+// share a SIMD overlap one's softmax with the other's MFMAs.  The four buffers
+// are distinct LDS objects and the loop is unrolled by buffer parity, so the
 // compiler can see that the loads in flight never alias the buffers read.
 // ---------------------------------------------------------------------------
 constexpr int TILE_BYTES = NKEY * D * 2;  // 16 KiB: one K or V tile
@@ -210,11 +207,16 @@ constexpr int DMA_ROWS = NKEY / NWAVE;    // tile rows each wave loads
 constexpr int DMA_INSTR = DMA_ROWS / 4;   // 1 KiB (4-row) load instructions per wave per tile
 static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divide the MFMAs");
 
+// Order of the 16 PV MFMAs: fragment f = 4*nb + kk feeds accumulator nb with
+// key step kk.  Going round-robin over the four accumulators keeps
+// consecutive MFMAs independent.
+__device__ __forceinline__ constexpr int pv_order(int i) { return 4 * (i & 3) + (i >> 2); }
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <bool HAS_DEPTH>
 __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
-  // A tile holds TQ = floor(128 / G) tokens x G heads; rows past TQ * G idle.
+  // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
   __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
@@ -264,6 +266,67 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] = 0.f;
   const float sc = p.scale_log2;
+
+  // ---------------- depth part: this wave's tokens' contiguous depth span.
+  // Odd workgroups stream their depth span before the key loop, even ones
+  // after it, so that at any time part of the chip streams depth blocks from
+  // HBM while the rest runs the matrix-core-bound key loop.
+  auto depth_part = [&]() {
+    if constexpr (HAS_DEPTH) {
+      const int64_t L = p.L;
+      const int64_t wt_lo = t0 + (wave * 32) / G;
+      int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;  // one past the wave's last token
+      if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
+      if (wt_hi > T) wt_hi = T;
+      if (L > 0 && wt_lo < wt_hi) {
+        const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
+        const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
+        const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
+        const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
+        u32x4 kd[8], vd[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          kd[ks] = *(const u32x4 *)(pk + blk_lo * kPackedBlockBytes + ks * 1024);
+        for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+          const char *kp = pk + blk * kPackedBlockBytes;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vd[j] = *(const u32x4 *)(kp + BLK_HALF + j * 1024);
+          floatx16 sd[1];
+          // two independent MFMA chains over the even and odd k-steps
+          floatx16 sd2[2] = {};
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            sd2[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, kd[ks]), qb[ks], sd2[ks & 1], 0, 0, 0);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
+          if (blk + 1 < blk_hi) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+              kd[ks] = *(const u32x4 *)(kp + kPackedBlockBytes + ks * 1024);
+          }
+          // entry of register rr: blk*32 + 8*(rr/4) + 4*lh + rr%4; keep it iff it
+          // belongs to this row's token
+          // (clamped to [-64, L]: every clamped value keeps the keep/drop decision)
+          int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
+          const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[0][rr] = -INFINITY;
+          bf16x8 pb[2];
+          softmax_update<1>(st, sd, p.scale_log2, pb);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, vd[nb * 2 + kk]), pb[kk], st.acc[nb], 0, 0, 0);
+        }
+      }
+    }
+  };
+  const bool depth_first = HAS_DEPTH && (blockIdx.x & 1);
+  if (depth_first) depth_part();
 
   // ---------------- sequence part
   const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
@@ -384,13 +447,14 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
     {
       bf16x8 a[3];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, i);
+      for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, pv_order(i));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        st.acc[i >> 2] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[i & 3], st.acc[i >> 2], 0, 0, 0);
-        if (i + 3 < 16) a[i % 3] = vfrag(v_rd, i + 3);
+        const int f = pv_order(i);
+        st.acc[f >> 2] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[f & 3], st.acc[f >> 2], 0, 0, 0);
+        if (i + 3 < 16) a[i % 3] = vfrag(v_rd, pv_order(i + 3));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -420,59 +484,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
     }
   }
 
-  // ---------------- depth part: this wave's tokens' contiguous depth span
-  if constexpr (HAS_DEPTH) {
-    const int64_t L = p.L;
-    const int64_t wt_lo = t0 + (wave * 32) / G;
-    int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;  // one past the wave's last token
-    if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
-    if (wt_hi > T) wt_hi = T;
-    if (L > 0 && wt_lo < wt_hi) {
-      const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
-      const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
-      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
-      const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
-      u32x4 kd[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        kd[ks] = *(const u32x4 *)(pk + blk_lo * kPackedBlockBytes + ks * 1024);
-      for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
-        const char *kp = pk + blk * kPackedBlockBytes;
-        u32x4 vd[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vd[j] = *(const u32x4 *)(kp + BLK_HALF + j * 1024);
-        floatx16 sd[1];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sd[0][rr] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          sd[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]),
-                                                          qb[ks], sd[0], 0, 0, 0);
-        if (blk + 1 < blk_hi) {
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            kd[ks] = *(const u32x4 *)(kp + kPackedBlockBytes + ks * 1024);
-        }
-        // entry of register rr: blk*32 + 8*(rr/4) + 4*lh + rr%4; keep it iff it
-        // belongs to this row's token
-        // (clamped to [-64, L]: every clamped value keeps the keep/drop decision)
-        int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
-        const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[0][rr] = -INFINITY;
-        bf16x8 pb[2];
-        softmax_update<1>(st, sd, p.scale_log2, pb);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, vd[nb * 2 + kk]), pb[kk], st.acc[nb], 0, 0, 0);
-      }
-    }
-  }
-
+  if (!depth_first) depth_part();
   MODA_TRACE(7);  // depth part
   MODA_TRACE_FLUSH;
   // ---------------- epilogue: the single normalisation
