@@ -230,6 +230,9 @@ def main():
                     help="with --sweep: run only points whose name contains this string")
     ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack"],
                     help="only launch this kernel (steps times) for counter collection")
+    ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
+                    help="time a bf16 N x N x N torch.matmul (hipBLASLt): the practical "
+                         "matrix-core rate of this GPU under its power limit, for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy a 1 GiB buffer (steps times): HBM counter calibration")
     args = ap.parse_args()
@@ -240,6 +243,27 @@ def main():
 
     from synth import WORKLOADS, sweep_points
 
+    if args.gemm_reference:
+        import torch
+        n = args.gemm_reference
+        a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+        b_ = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(max(args.warmup, 1)):
+            c = a @ b_
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            c = a @ b_
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        del c
+        print(json.dumps({"gemm": f"bf16 {n}x{n}x{n} torch.matmul", "ms": ms,
+                          "tflops": 2.0 * n ** 3 / ms / 1e9,
+                          "pct_bf16_peak": 100.0 * 2.0 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS}),
+              flush=True)
+        return
     if args.copy_calibration:
         import torch
         n = 1 << 30
