@@ -73,9 +73,6 @@ constexpr int D = kMfmaD;             // 128
 constexpr int M = kMfmaRows;          // 256 query rows per workgroup
 constexpr int NKEY = 64;              // keys per sequence tile
 constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
-// The reference max of a row moves only when a new score exceeds it by more
-// than 2^8: weights stay <= 256, exact in fp32 and as bf16 operands.
-constexpr float RESCALE_SLACK = 8.0f;
 
 typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
@@ -137,34 +134,11 @@ struct MfmaState {
   floatx16 acc[4];  // O^T accumulator: 4 blocks of 32 head-dim rows
 };
 
-// Online-softmax update for NB score blocks of 32 entries each (already
-// masked with -inf): move the reference max if needed, turn scores into
-// weights and return them as bf16 B operands, pb[2*i + {0,1}] for block i.
+// Weights 2^(s * scale_log2 - m) of NB score blocks as bf16 B operands,
+// pb[2*i + {0,1}] for block i, and their sum (this lane's share of the row).
 template <int NB>
-__device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s, float scale_log2,
-                                               bf16x8 *pb) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-  const float mt = pair_max(mx) * scale_log2;
-  // The branch is wave-wide, but each row moves its reference only when its
-  // own scores ask for it (alpha is exactly 1 otherwise), so a row's result
-  // never depends on the other rows of the wave.
-  const bool need = mt > st.m + RESCALE_SLACK;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? mt : st.m;
-    const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
-    st.m = m_new;
-    st.lsum *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
-  }
-  // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
-  const float neg_m = st.m == -INFINITY ? 0.f : -st.m;
+__device__ __forceinline__ float tile_weights(const floatx16 *s, float scale_log2, float neg_m,
+                                              bf16x8 *pb) {
   float sum = 0.f;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -178,6 +152,46 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
     }
     pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
     pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
+  }
+  return sum;
+}
+
+// A row's weights in one tile may sum to at most this much before the row
+// moves its reference max; every weight stays <= 2^12.
+constexpr float TILE_SUM_LIMIT = 4096.0f;
+
+// Online-softmax update for NB score blocks of 32 entries each (already
+// masked with -inf): turn scores into weights against the row's reference
+// max and return them as bf16 B operands, pb[2*i + {0,1}] for block i.
+// The weights are first taken against the current reference.  A row with no
+// reference yet, or whose weights in this tile sum past TILE_SUM_LIMIT, moves
+// its reference to the tile's max, rescales its state and takes its weights
+// again.  The branch is wave-wide, but each row decides from its own scores and
+// a row that does not move recomputes exactly the same weights, so a row's
+// result never depends on the other rows of the wave.
+template <int NB>
+__device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s, float scale_log2,
+                                               bf16x8 *pb) {
+  const bool fresh = st.m == -INFINITY;
+  float sum = tile_weights<NB>(s, scale_log2, fresh ? 0.f : -st.m, pb);
+  const bool need = fresh || !(pair_sum(sum) <= TILE_SUM_LIMIT);
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+    const float mt = pair_max(mx) * scale_log2;
+    const float m_new = need ? fmaxf(mt, st.m) : st.m;
+    const float alpha = m_new == st.m ? 1.0f : fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+    // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
+    sum = tile_weights<NB>(s, scale_log2, st.m == -INFINITY ? 0.f : -st.m, pb);
   }
   st.lsum += sum;
 }

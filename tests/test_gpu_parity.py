@@ -134,6 +134,41 @@ def test_depth_heavy_sampled(m, dev):
     sampled_check(m, WORKLOADS["depth_heavy"], dev)
 
 
+def adversarial_inputs(kind, B=1, Hq=8, Hkv=2, T=700, L=5, seed=21):
+    """bf16 inputs whose scores force the online softmax to move its reference
+    max often: sequence scores that rise (or fall) steeply along the key axis,
+    and depth entries that dominate every even token's row."""
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    d = 128
+    j = np.arange(T, dtype=np.float64)
+    s = 0.05 + 8.0 * j / T if kind == "rising" else 8.0 - 7.9 * j / T
+    q = rng.standard_normal((B, Hq, T, d)) * 0.5 + 1.0
+    k = (rng.standard_normal((B, Hkv, T, d)) * 0.5 + 1.0) * s[None, None, :, None]
+    v = rng.standard_normal((B, Hkv, T, d))
+    kd = rng.standard_normal((B, Hkv, T, L, d)) * 0.5 + 1.0
+    kd *= np.where(np.arange(T) % 2 == 0, 10.0, 0.1)[None, None, :, None, None]
+    vd = rng.standard_normal((B, Hkv, T, L, d))
+    return {n: f32_to_bf16_bits(a.astype(np.float32))
+            for n, a in dict(q=q, k=k, v=v, kd=kd, vd=vd).items()}
+
+
+@pytest.mark.parametrize("kind,Hq,Hkv", [("rising", 8, 2), ("falling", 8, 2), ("rising", 4, 4),
+                                         ("rising", 32, 4)])
+def test_rescale_paths(m, dev, kind, Hq, Hkv):
+    """Steep score ramps and dominant depth entries: many reference-max moves
+    inside the key loop and in the depth part, against the oracle."""
+    from gpu_util import to_dev
+    h = adversarial_inputs(kind, Hq=Hq, Hkv=Hkv)
+    d_in = {n: to_dev(a, "bf16", dev) for n, a in h.items()}
+    out, lse = run_full(m, d_in, 5)
+    ref, rlse = oracle.moda_forward(h["q"], h["k"], h["v"], h["kd"], h["vd"])
+    e_o, e_l = max_err(out_to_f64(out), ref), max_err(lse.cpu().numpy(), rlse)
+    print(f"[parity] rescale {kind} Hq{Hq} Hkv{Hkv} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}",
+          flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_l0_equals_causal_bitwise(m, dev):
