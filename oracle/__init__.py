@@ -10,7 +10,9 @@ What it computes is the plain definition of Mixture-of-Depths Attention
 scaled by 1/sqrt(d), over the causal sequence keys 0..t of KV head h // G and
 the L depth keys of token t, followed by the weighted sum of the matching
 values.  ``moda_oracle.c`` writes the steps out; this module builds it with
-gcc and marshals arrays through ctypes.
+gcc and marshals arrays through ctypes.  ``depth_forward`` is depth attention
+alone (same page, section "Depth stream mechanism"): each query row over its
+own token's L depth entries only.
 
 Every function here has pins in ``tests/test_oracle_pins.py``; none is
 "parity unpinned".
@@ -58,6 +60,8 @@ def load(path: str | None = None):
     lib.oracle_moda_row_weights.argtypes = ([i64] * 6 + [ctypes.c_int] + [i64] * 3 +
                                             [vp] * 5 + [dp, dp])
     lib.oracle_moda_row_weights.restype = ctypes.c_int
+    lib.oracle_depth_fwd.argtypes = [i64] * 6 + [ctypes.c_int] + [vp] * 3 + [dp, dp]
+    lib.oracle_depth_fwd.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
@@ -165,6 +169,28 @@ def moda_row_weights(q, k, v, kd, vd, b, h, t, *, lib=None):
     if rc:
         raise ValueError(f"oracle_moda_row_weights failed with code {rc}")
     return p, o
+
+
+def depth_forward(q, kd, vd, *, lib=None):
+    """fp64 depth attention alone: each query row over its own token's L depth
+    entries, one softmax scaled by 1/sqrt(d) (no sequence keys).
+
+    q [B,Hq,T,d]; kd, vd [B,Hkv,T,L,d] with L >= 1, same element type as q.
+    Returns (out [B,Hq,T,d] float64, lse [B,Hq,T] float64).
+    """
+    lib = lib or load()
+    code = _code_of(q)
+    B, Hq, T, d = q.shape
+    Hkv, L = kd.shape[1], kd.shape[3]
+    q, kd, vd = (_as_input(x, code) for x in (q, kd, vd))
+    assert kd.shape == (B, Hkv, T, L, d) and vd.shape == kd.shape
+    out = np.empty((B, Hq, T, d), np.float64)
+    lse = np.empty((B, Hq, T), np.float64)
+    rc = lib.oracle_depth_fwd(B, Hq, Hkv, T, L, d, code, _ptr(q), _ptr(kd), _ptr(vd),
+                              _ptr(out), _ptr(lse))
+    if rc:
+        raise ValueError(f"oracle_depth_fwd failed with code {rc}")
+    return out, lse
 
 
 def num_threads(*, lib=None) -> int:

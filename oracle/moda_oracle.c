@@ -230,3 +230,57 @@ int oracle_num_threads(void) {
   }
   return n;
 }
+
+/*
+ * Depth attention alone: the read step of the depth stream (hyper.ai summary
+ * of arXiv 2603.15619, section "Depth stream mechanism": the input of layer l
+ * comes from attention over the keys and values {K_i, V_i}, i = 0..l-1, that
+ * the preceding layers left at the same token position).  The query row of
+ * token t attends over its own token's L depth entries and nothing else,
+ * under one softmax scaled by 1/sqrt(d):
+ *   1. c_i = sd * <q_t, Kd_{t,i}>          for i = 0..L-1
+ *   2. mx = max c ; w_i = exp(c_i - mx) ; Zd = sum w ; p_i = w_i / Zd
+ *   3. o_t = sum_i p_i Vd_{t,i} ;  lse = mx + ln Zd
+ *   q [B,Hq,T,d]  kd, vd [B,Hkv,T,L,d] (L >= 1)
+ *   out [B,Hq,T,d] double;  lse [B,Hq,T] double (may be NULL)
+ * Returns 0 on success, nonzero on a bad shape or an allocation failure.
+ */
+int oracle_depth_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t L,
+                     int64_t d, int dtype, const void *q, const void *kd,
+                     const void *vd, double *out, double *lse) {
+  if (bad_shape(B, Hq, Hkv, T, L, d, dtype) || L < 1) return 1;
+  const int64_t grp = Hq / Hkv;
+  const int64_t nrows = B * Hq * T;
+  const double sd = 1.0 / sqrt((double)d);
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *c = (double *)malloc((size_t)L * sizeof(double));
+    if (!c) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t t = r % T, h = (r / T) % Hq, b = r / (T * Hq);
+        const int64_t own = ((b * Hkv + h / grp) * T + t) * L * d;  /* token t's entries */
+        for (int64_t i = 0; i < L; ++i) c[i] = sd * dot(q, r * d, kd, own + i * d, d, dtype);
+        double mx = c[0];
+        for (int64_t i = 1; i < L; ++i) mx = c[i] > mx ? c[i] : mx;
+        double Zd = 0.0;
+        for (int64_t i = 0; i < L; ++i) {
+          c[i] = exp(c[i] - mx);
+          Zd += c[i];
+        }
+        for (int64_t col = 0; col < d; ++col) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < L; ++i) acc += (c[i] / Zd) * elem(vd, own + i * d + col, dtype);
+          out[r * d + col] = acc;
+        }
+        if (lse) lse[r] = mx + log(Zd);
+      }
+      free(c);
+    }
+  }
+  return failed ? 2 : 0;
+}

@@ -38,3 +38,22 @@ def moda_bruteforce(q, k, v, kd=None, vd=None):
         out = out + np.einsum("bhtl,bhtld->bhtd", p[..., T:], vde)
     lse = (m + np.log(Z))[..., 0]
     return out, lse
+
+
+def depth_bruteforce(q, kd, vd):
+    """Depth attention alone in matrix form (NumPy fp64): scores
+    s*<q_t, Kd_{t,i}> over the L entries of token t, softmax along i, then the
+    weighted sum of Vd_{t,i}.  Same definition as the oracle's depth
+    attention (hyper.ai page on arXiv 2603.15619, section "Depth stream
+    mechanism"), written with einsum over whole tensors."""
+    q = np.asarray(q, np.float64)
+    B, Hq, T, d = q.shape
+    G = Hq // kd.shape[1]
+    kde = np.repeat(np.asarray(kd, np.float64), G, axis=1)
+    vde = np.repeat(np.asarray(vd, np.float64), G, axis=1)
+    sc = np.einsum("bhtd,bhtld->bhtl", q, kde) / np.sqrt(d)
+    m = sc.max(axis=-1, keepdims=True)
+    w = np.exp(sc - m)
+    Z = w.sum(axis=-1, keepdims=True)
+    out = np.einsum("bhtl,bhtld->bhtd", w / Z, vde)
+    return out, (m + np.log(Z))[..., 0]

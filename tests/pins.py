@@ -16,6 +16,9 @@ Sources of the facts:
   * the causal sequence part alone is ordinary causal attention, a library
     routine.  -> pin a
   * a second formulation in another language (tests/bruteforce.py).  -> pin e
+  * same page, section "Depth stream mechanism": depth attention alone reads
+    the token's own depth entries under one softmax.  -> pins o to s (the
+    oracle's standalone depth attention)
 """
 from __future__ import annotations
 
@@ -24,7 +27,7 @@ import math
 import numpy as np
 
 import oracle
-from bruteforce import moda_bruteforce
+from bruteforce import depth_bruteforce, moda_bruteforce
 from synth import bf16_bits_to_f32, f32_to_bf16_bits
 
 TOL = 1e-12
@@ -295,6 +298,88 @@ def pin_n_rows_entry(lib):
     o2, l2 = oracle.moda_rows(rows, (B, Hq, Hkv, T, L, d), qr, k, v, kdr, vdr, lib=lib)
     for i, (b, h, t) in enumerate(rows):
         assert np.array_equal(o2[i], out[b, h, t]) and l2[i] == lse[b, h, t]
+
+
+def _depth(lib, q, kd, vd):
+    return oracle.depth_forward(q, kd, vd, lib=lib)
+
+
+def pin_o_depth_hand_example(lib):
+    """Depth attention alone, worked by hand (d=1, T=2, L=2, one head).
+
+    token 0: logits [1.5*0.5, 1.5*(-1)] = [0.75, -1.5], values [2, -3]
+    token 1: logits [-0.5*2, -0.5*1] = [-1, -0.5], values [1, 4]
+    """
+    q = np.array([[1.5], [-0.5]])[None, None]
+    kd = np.array([[[0.5], [-1.0]], [[2.0], [1.0]]])[None, None]
+    vd = np.array([[[2.0], [-3.0]], [[1.0], [4.0]]])[None, None]
+    out, lse = _depth(lib, q, kd, vd)
+    a, b = math.exp(0.75), math.exp(-1.5)
+    c, e = math.exp(-1.0), math.exp(-0.5)
+    _close(out[0, 0, :, 0], [(2 * a - 3 * b) / (a + b), (c + 4 * e) / (c + e)],
+           what="depth hand example")
+    _close(lse[0, 0], [math.log(a + b), math.log(c + e)], what="depth hand example lse")
+
+
+def pin_p_depth_bruteforce(lib):
+    """Depth attention alone against the NumPy matrix form, including GQA,
+    one entry, and fp32 / bf16 inputs read exactly."""
+    for (B, Hq, Hkv, T, L, d, seed) in [(1, 2, 1, 7, 3, 8, 131), (2, 8, 2, 5, 1, 4, 132),
+                                        (1, 4, 4, 3, 17, 16, 133), (1, 6, 3, 9, 5, 32, 134)]:
+        q, _, _, kd, vd = _case(B, Hq, Hkv, T, L, d, seed)
+        out, lse = _depth(lib, q, kd, vd)
+        ref, rlse = depth_bruteforce(q, kd, vd)
+        _close(out, ref, what=f"depth bruteforce {B,Hq,Hkv,T,L,d}")
+        _close(lse, rlse, what=f"depth bruteforce lse {B,Hq,Hkv,T,L,d}")
+    q, _, _, kd, vd = _case(1, 4, 2, 6, 4, 8, 135)
+    for enc, dec in ((lambda x: x.astype(np.float32), lambda x: x.astype(np.float64)),
+                     (lambda x: f32_to_bf16_bits(x.astype(np.float32)),
+                      lambda x: bf16_bits_to_f32(x).astype(np.float64))):
+        xs = [enc(x) for x in (q, kd, vd)]
+        out, lse = _depth(lib, *xs)
+        ref, rlse = depth_bruteforce(*(dec(x) for x in xs))
+        _close(out, ref, what="depth bruteforce, narrow inputs")
+        _close(lse, rlse, what="depth bruteforce lse, narrow inputs")
+
+
+def pin_q_depth_merge(lib):
+    """MoDA is the log-sum-exp merge of causal attention and depth attention
+    alone: ties the standalone depth attention to the MoDA oracle."""
+    B, Hq, Hkv, T, L, d = 2, 6, 2, 9, 4, 8
+    q, k, v, kd, vd = _case(B, Hq, Hkv, T, L, d, 141)
+    out, lse = _fwd(lib, q, k, v, kd, vd)
+    o_s, l_s = _fwd(lib, q, k, v, None, None)
+    o_d, l_d = _depth(lib, q, kd, vd)
+    mm = np.maximum(l_s, l_d)
+    a, c = np.exp(l_s - mm), np.exp(l_d - mm)
+    _close(out, (a[..., None] * o_s + c[..., None] * o_d) / (a + c)[..., None],
+           what="causal + depth merge")
+    _close(lse, mm + np.log(a + c), what="causal + depth merge lse")
+
+
+def pin_r_depth_single_entry(lib):
+    """With one depth entry its weight is exactly 1: O_t = Vd[t, 0] bit for
+    bit, and LSE is that entry's logit."""
+    B, Hq, Hkv, T, L, d = 1, 4, 2, 5, 1, 8
+    q, _, _, kd, vd = _case(B, Hq, Hkv, T, L, d, 151)
+    out, lse = _depth(lib, q, kd, vd)
+    G = Hq // Hkv
+    assert np.array_equal(out, np.repeat(vd[:, :, :, 0], G, axis=1)), "single depth entry"
+    logit = np.einsum("bhtd,bhtd->bht", q, np.repeat(kd[:, :, :, 0], G, axis=1)) / math.sqrt(d)
+    _close(lse, logit, what="single depth entry lse")
+
+
+def pin_s_depth_dominance(lib):
+    """A depth key aligned with the query with a logit of 1000 (exp of it
+    overflows a double) takes all the weight: O_t = Vd[t, i*]."""
+    B, Hq, Hkv, T, L, d = 1, 1, 1, 5, 3, 8
+    q, _, _, kd, vd = _case(B, Hq, Hkv, T, L, d, 161)
+    kd = kd.copy()
+    lam = 1000.0 * math.sqrt(d) / (q[0, 0] ** 2).sum(-1)
+    kd[0, 0, :, 1] = lam[:, None] * q[0, 0]
+    out, lse = _depth(lib, q, kd, vd)
+    _close(out[0, 0], vd[0, 0, :, 1], tol=1e-12, what="depth dominance")
+    _close(lse[0, 0], np.full(T, 1000.0), tol=1e-9, what="depth dominance lse")
 
 
 PINS = [(name, fn) for name, fn in sorted(globals().items()) if name.startswith("pin_")]

@@ -33,6 +33,18 @@ MUTANTS = [
     ("bf16_shift", "<< 16;", "<< 15;", 1),
     ("depth_sign", "x[t + 1 + i] = s * dot(", "x[t + 1 + i] = -s * dot(", 1),
     ("value_from_key", "acc += x[j] * elem(v,", "acc += x[j] * elem(k,", 1),
+    # standalone depth attention
+    ("depth_only_no_scale", "const double sd = 1.0 / sqrt((double)d);", "const double sd = 1.0;",
+     1),
+    ("depth_only_prev_token", "const int64_t own = ((b * Hkv + h / grp) * T + t) * L * d;",
+     "const int64_t own = ((b * Hkv + h / grp) * T + (t > 0 ? t - 1 : 0)) * L * d;", 1),
+    ("depth_only_head_modulo", "(b * Hkv + h / grp)", "(b * Hkv + h % Hkv)", 1),
+    ("depth_only_no_max_shift", "c[i] = exp(c[i] - mx);", "c[i] = exp(c[i]);", 1),
+    ("depth_only_values_from_keys", "elem(vd, own + i * d + col, dtype)",
+     "elem(kd, own + i * d + col, dtype)", 1),
+    ("depth_only_lse_no_max", "if (lse) lse[r] = mx + log(Zd);", "if (lse) lse[r] = log(Zd);",
+     1),
+    ("depth_only_unnormalised", "acc += (c[i] / Zd) *", "acc += c[i] *", 1),
 ]
 
 
