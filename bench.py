@@ -4,7 +4,8 @@
 One step = the whole MoDA path over one batch of synthetic input already in
 HBM: moda_pack_depth_cache (depth repack) + moda_fwd (fused forward).  The
 causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
-MoDA / causal-only time ratio.  Prints one JSON line.
+MoDA / causal-only time ratio, and depth attention alone (moda_depth_fwd) on
+the same packed cache for its HBM rate.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
@@ -47,6 +48,12 @@ def fused_bytes(c, L=None):
     L = c["L"] if L is None else L
     B, Hq, Hkv, T, d = c["B"], c["Hq"], c["Hkv"], c["T"], c["d"]
     return es(c) * (2 * B * Hq * T * d + 2 * B * Hkv * T * d + 2 * B * Hkv * T * L * d)
+
+
+def depth_bytes(c):
+    """Depth attention alone: Q and O once, depth K/V once (no LSE)."""
+    B, Hq, Hkv, T, L, d = c["B"], c["Hq"], c["Hkv"], c["T"], c["L"], c["d"]
+    return es(c) * (2 * B * Hq * T * d + 2 * B * Hkv * T * L * d)
 
 
 def pack_bytes(c):
@@ -187,7 +194,14 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True):
         cout = torch.empty_like(q)
         moda.causal_fwd(q, k, v, out=cout)
         causal_ms = float(np.mean(timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream)))
-    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms)
+    depth_ms = None
+    if L:
+        dout = torch.empty_like(q)
+        moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout)
+        depth_ms = float(np.mean(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
+                                       steps, stream)))
+    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
+               depth_ms=depth_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -212,6 +226,8 @@ def profile_only(cfg, which, steps):
             moda.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, out=out)
         elif which == "causal":
             moda.causal_fwd(d_in["q"], d_in["k"], d_in["v"], out=out)
+        elif which == "depth":
+            moda.depth_fwd(d_in["q"], packed, cfg["Hkv"], L, out=out)
         else:
             moda.pack_depth_cache(d_in["kd"], d_in["vd"], shape, out=packed)
     torch.cuda.synchronize()
@@ -228,7 +244,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--only", default=None,
                     help="with --sweep: run only points whose name contains this string")
-    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack"],
+    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
                     help="time a bf16 N x N x N torch.matmul (hipBLASLt): the practical "
@@ -302,7 +318,10 @@ def main():
                               "fwd_tflops": flops(c) / r["fwd_ms"] / 1e9,
                               "causal_tflops": flops(c, 0) / r["causal_ms"] / 1e9,
                               "ratio_fwd_over_causal": r["fwd_ms"] / r["causal_ms"],
-                              "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6}), flush=True)
+                              "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6,
+                              "depth_only_ms": r["depth_ms"],
+                              "depth_only_hbm_gbs": (depth_bytes(c) / r["depth_ms"] / 1e6
+                                                     if r["depth_ms"] else None)}), flush=True)
         return
 
     cfg = dict(named[args.config])
@@ -338,6 +357,8 @@ def main():
         "ratio_step_over_causal": step_ms / r["causal_ms"],
         "pack_hbm_gbs": pack_bytes(cfg) / r["pack_ms"] / 1e6 if r["pack_ms"] else None,
         "fwd_hbm_gbs": fused_bytes(cfg) / r["fwd_ms"] / 1e6,
+        "depth_only_ms": r["depth_ms"],
+        "depth_only_hbm_gbs": depth_bytes(cfg) / r["depth_ms"] / 1e6 if r["depth_ms"] else None,
         "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:

@@ -98,7 +98,8 @@ moda_status hip_status(hipError_t e, const char *what) {
 }
 
 moda::FwdArgs make_fwd_args(const moda_shape *s, const void *q, const void *k, const void *v,
-                            const void *packed, void *out, float *lse, bool has_depth) {
+                            const void *packed, void *out, float *lse, bool has_depth,
+                            bool has_seq = true) {
   moda::FwdArgs a{};
   a.q = q;
   a.k = k;
@@ -115,7 +116,18 @@ moda::FwdArgs make_fwd_args(const moda_shape *s, const void *q, const void *k, c
   a.nblk = depth_blocks(s);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
   a.has_depth = has_depth && s->L > 0;
+  a.has_seq = has_seq;
   return a;
+}
+
+moda_status check_packed(const moda_shape *s, const void *packed, size_t packed_bytes) {
+  if (!packed) return fail(MODA_ERR_INVALID_ARG, "packed must be non-NULL when L > 0");
+  if (!aligned16(packed)) return fail(MODA_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  const size_t need = cache_bytes(s);
+  if (packed_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(packed_bytes));
+  return MODA_OK;
 }
 
 moda_status check_qkvo(const void *q, const void *k, const void *v, const void *out,
@@ -176,12 +188,8 @@ moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const vo
   st = check_qkvo(q, k, v, out, lse);
   if (st != MODA_OK) return st;
   if (s->L > 0) {
-    if (!packed) return fail(MODA_ERR_INVALID_ARG, "packed must be non-NULL when L > 0");
-    if (!aligned16(packed)) return fail(MODA_ERR_INVALID_ARG, "packed must be 16-byte aligned");
-    const size_t need = cache_bytes(s);
-    if (packed_bytes < need)
-      return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
-                                            " bytes, got " + std::to_string(packed_bytes));
+    st = check_packed(s, packed, packed_bytes);
+    if (st != MODA_OK) return st;
   } else if (packed || packed_bytes) {
     return fail(MODA_ERR_INVALID_ARG, "packed must be NULL with size 0 when L == 0");
   }
@@ -206,6 +214,23 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, c
   if (use_mfma(&s0))
     return hip_status(moda::launch_fwd_mfma(a, (int)(s0.Hq / s0.Hkv), stream), "causal launch");
   return hip_status(moda::launch_fwd_generic(a, s0.dtype == MODA_BF16, stream), "causal launch");
+}
+
+moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packed,
+                           size_t packed_bytes, void *out, float *lse, void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_depth_fwd needs L >= 1");
+  if (!q || !out) return fail(MODA_ERR_INVALID_ARG, "q and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  st = check_packed(s, packed, packed_bytes);
+  if (st != MODA_OK) return st;
+  moda::FwdArgs a = make_fwd_args(s, q, nullptr, nullptr, packed, out, lse, true, false);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (use_mfma(s))
+    return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), stream), "depth launch");
+  return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "depth launch");
 }
 
 const char *moda_status_string(moda_status st) {

@@ -20,8 +20,14 @@ struct FwdArgs {
   int64_t B, Hq, Hkv, T, L, d;
   int64_t nblk;   // packed depth blocks per (b, kv head) (MFMA path)
   float scale_log2;  // log2(e) / sqrt(d)
-  bool has_depth;
+  bool has_depth;  // the token's depth entries join the softmax
+  bool has_seq;    // the causal sequence keys join the softmax
 };
+
+// Kernel modes: causal attention, MoDA (sequence + depth), depth attention alone.
+constexpr int kModeCausal = 0;
+constexpr int kModeModa = 1;
+constexpr int kModeDepth = 2;
 
 struct PackArgs {
   const void *kd, *vd;

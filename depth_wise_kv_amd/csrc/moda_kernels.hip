@@ -228,8 +228,10 @@ __device__ __forceinline__ constexpr int pv_order(int i) { return 4 * (i & 3) + 
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <bool HAS_DEPTH>
+template <int MODE>
 __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
+  constexpr bool HAS_DEPTH = MODE != kModeCausal;  // depth entries are read
+  constexpr bool HAS_SEQ = MODE != kModeDepth;     // sequence keys are read
   // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
@@ -339,162 +341,164 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
       }
     }
   };
-  const bool depth_first = HAS_DEPTH && (blockIdx.x & 1);
+  const bool depth_first = HAS_DEPTH && (!HAS_SEQ || (blockIdx.x & 1));
+  MODA_TRACE_DECL
   if (depth_first) depth_part();
 
-  // ---------------- sequence part
-  const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
-  const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
-  const int64_t wave_tok_lo = t0 + (wave * 32) / G;
+  if constexpr (HAS_SEQ) {
+    // ---------------- sequence part
+    const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
+    const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
+    const int64_t wave_tok_lo = t0 + (wave * 32) / G;
 
-  // direct loads: instruction i of this wave fills tile rows 16*wave + 4i .. +3.
-  // Buffer descriptors cover one (b, kv head) of K and of V; the tile offset
-  // goes in the scalar offset, the lane's row/chunk in the vector offset.
-  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const char *)p.k + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
-  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const char *)p.v + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
-  const int dma_row = DMA_ROWS * wave + (lane >> 4);  // + 4i
-  uint32_t dk_off[DMA_INSTR], dv_off[DMA_INSTR];
+    // direct loads: instruction i of this wave fills tile rows 16*wave + 4i .. +3.
+    // Buffer descriptors cover one (b, kv head) of K and of V; the tile offset
+    // goes in the scalar offset, the lane's row/chunk in the vector offset.
+    const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)p.k + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)p.v + bh * T * (D * 2)), (short)0, (int)(T * (D * 2)), 0x00020000);
+    const int dma_row = DMA_ROWS * wave + (lane >> 4);  // + 4i
+    uint32_t dk_off[DMA_INSTR], dv_off[DMA_INSTR];
 #pragma unroll
-  for (int i = 0; i < DMA_INSTR; ++i) {
-    const int row = dma_row + 4 * i;
-    dk_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (row & 15)));
-    dv_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3))));
-  }
-  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, char *lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
-                                             16, voff, soff, 0, 0);
-  };
-  // instruction q of this wave's 2*DMA_INSTR loads of tile kt: q < DMA_INSTR
-  // loads K rows, the rest V rows.  Rows at or past T fall outside the descriptor's range and read as
-  // zeros, which every mask removes.
-  auto dma_one = [&](int q, int kt, char *k_dst, char *v_dst) {
-    const uint32_t soff = (uint32_t)kt * TILE_BYTES;
-    const int i = q % DMA_INSTR;
-    if (q < DMA_INSTR) dma(k_rsrc, k_dst + wave * DMA_ROWS * 256 + i * 1024, dk_off[i], soff);
-    else dma(v_rsrc, v_dst + wave * DMA_ROWS * 256 + i * 1024, dv_off[i], soff);
-  };
-  // MFMA operand reads.  K: row 32*kb2 + li, chunk 8*lh + ks, in slot
-  // (8*lh + ks) ^ (li % 16) = (8*lh ^ (li & 8)) + (ks ^ (li & 7)).
-  const int k_row = li * 256 + 16 * ((8 * lh) ^ (li & 8));
-  const int k_x = li & 7;
-  // V (transpose reads): lane group lg = lane/16 and lq = lane%16 read key row
-  // 16*kk + 8*hi + 4*(lg/2) + lq/4, dims 32*nb + 16*(lg%2) + 4*(lq%4) .. +3.
-  const int lg = lane >> 4, lq = lane & 15;
-  int vaddr[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    vaddr[nb] = (4 * (lg >> 1) + (lq >> 2)) * 256 +
-                16 * (4 * (nb ^ (lq >> 2)) + 2 * (lg & 1) + ((lq & 3) >> 1)) + 8 * (lq & 1);
-
-  auto kfrag = [&](const char *kb, int i) {  // i = 2*ks + kb2
-    return *(const bf16x8 *)(kb + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
-  };
-  auto vfrag = [&](const char *vb, int i) {  // i = 4*nb + kk
-    const char *vp = vb + vaddr[i >> 2] + 16 * (i & 3) * 256;
-    const shortx4 lo = lds_read_tr(vp);
-    const shortx4 hi = lds_read_tr(vp + 8 * 256);
-    return __builtin_bit_cast(
-        bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-  };
-  auto mask = [&](floatx16 (&s)[2], int kt) {
-    // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
-    const int lim = (int)max((int64_t)-8, min((int64_t)64, tok - (int64_t)kt * NKEY - 4 * lh));
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
-  };
-
-  MODA_TRACE_DECL
-  // start from zeroed buffers: loads of rows past T may leave LDS untouched
-  for (int o = tid * 16; o < TILE_BYTES; o += 64 * NWAVE * 16) {
-    *(u32x4 *)(k_lds0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(k_lds1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(v_lds0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(v_lds1 + o) = u32x4{0, 0, 0, 0};
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 2 * DMA_INSTR; ++q) dma_one(q, 0, k_lds0, v_lds0);
-  wait_vmem();
-  __syncthreads();
-  MODA_TRACE(0);  // prologue
-
-  // iteration j with buffer parity P = j % 2: loads tile j+1 into the other
-  // buffers (last read in iteration j-1), computes tile j
-  auto body = [&](int j, auto parity, auto masked) {
-    constexpr int P = decltype(parity)::value;
-    const char *const k_rd = P ? k_lds1 : k_lds0;
-    const char *const v_rd = P ? v_lds1 : v_lds0;
-    char *const k_wr = P ? k_lds0 : k_lds1;
-    char *const v_wr = P ? v_lds0 : v_lds1;
-    MODA_TRACE(1);  // (loads are issued inside the QK^T sequence)
-    // S^T = K Q^T: the two 32-key chains alternate, K fragments are read four
-    // MFMAs ahead and the eight loads of tile j+1 are spread between the
-    // MFMAs; sched_barrier fences keep this order.
-    floatx16 s[2];
-    {
-      bf16x8 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = kfrag(k_rd, i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ks = i >> 1, kb2 = i & 1;
-        const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], qb[ks], c, 0, 0, 0);
-        if (i + 4 < 16) a[i & 3] = kfrag(k_rd, i + 4);
-        if (i % (16 / (2 * DMA_INSTR)) == 0) dma_one(i / (16 / (2 * DMA_INSTR)), j + 1, k_wr, v_wr);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < DMA_INSTR; ++i) {
+      const int row = dma_row + 4 * i;
+      dk_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (row & 15)));
+      dv_off[i] = (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3))));
     }
-    MODA_TRACE(2);  // QK^T
-    if constexpr (decltype(masked)::value) mask(s, j);
-    bf16x8 pb[4];
-    softmax_update<2>(st, s, sc, pb);
-    MODA_TRACE(3);  // mask + softmax
-    // O^T += V^T P^T: V fragments (two transpose reads each) three MFMAs ahead
-    {
-      bf16x8 a[3];
+    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, char *lds, uint32_t voff, uint32_t soff) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
+                                               16, voff, soff, 0, 0);
+    };
+    // instruction q of this wave's 2*DMA_INSTR loads of tile kt: q < DMA_INSTR
+    // loads K rows, the rest V rows.  Rows at or past T fall outside the descriptor's range and read as
+    // zeros, which every mask removes.
+    auto dma_one = [&](int q, int kt, char *k_dst, char *v_dst) {
+      const uint32_t soff = (uint32_t)kt * TILE_BYTES;
+      const int i = q % DMA_INSTR;
+      if (q < DMA_INSTR) dma(k_rsrc, k_dst + wave * DMA_ROWS * 256 + i * 1024, dk_off[i], soff);
+      else dma(v_rsrc, v_dst + wave * DMA_ROWS * 256 + i * 1024, dv_off[i], soff);
+    };
+    // MFMA operand reads.  K: row 32*kb2 + li, chunk 8*lh + ks, in slot
+    // (8*lh + ks) ^ (li % 16) = (8*lh ^ (li & 8)) + (ks ^ (li & 7)).
+    const int k_row = li * 256 + 16 * ((8 * lh) ^ (li & 8));
+    const int k_x = li & 7;
+    // V (transpose reads): lane group lg = lane/16 and lq = lane%16 read key row
+    // 16*kk + 8*hi + 4*(lg/2) + lq/4, dims 32*nb + 16*(lg%2) + 4*(lq%4) .. +3.
+    const int lg = lane >> 4, lq = lane & 15;
+    int vaddr[4];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, pv_order(i));
-      __builtin_amdgcn_sched_barrier(0);
+    for (int nb = 0; nb < 4; ++nb)
+      vaddr[nb] = (4 * (lg >> 1) + (lq >> 2)) * 256 +
+                  16 * (4 * (nb ^ (lq >> 2)) + 2 * (lg & 1) + ((lq & 3) >> 1)) + 8 * (lq & 1);
+
+    auto kfrag = [&](const char *kb, int i) {  // i = 2*ks + kb2
+      return *(const bf16x8 *)(kb + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
+    };
+    auto vfrag = [&](const char *vb, int i) {  // i = 4*nb + kk
+      const char *vp = vb + vaddr[i >> 2] + 16 * (i & 3) * 256;
+      const shortx4 lo = lds_read_tr(vp);
+      const shortx4 hi = lds_read_tr(vp + 8 * 256);
+      return __builtin_bit_cast(
+          bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+    };
+    auto mask = [&](floatx16 (&s)[2], int kt) {
+      // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
+      const int lim = (int)max((int64_t)-8, min((int64_t)64, tok - (int64_t)kt * NKEY - 4 * lh));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int f = pv_order(i);
-        st.acc[f >> 2] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[f & 3], st.acc[f >> 2], 0, 0, 0);
-        if (i + 3 < 16) a[i % 3] = vfrag(v_rd, pv_order(i + 3));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
+    };
+
+    // start from zeroed buffers: loads of rows past T may leave LDS untouched
+    for (int o = tid * 16; o < TILE_BYTES; o += 64 * NWAVE * 16) {
+      *(u32x4 *)(k_lds0 + o) = u32x4{0, 0, 0, 0};
+      *(u32x4 *)(k_lds1 + o) = u32x4{0, 0, 0, 0};
+      *(u32x4 *)(v_lds0 + o) = u32x4{0, 0, 0, 0};
+      *(u32x4 *)(v_lds1 + o) = u32x4{0, 0, 0, 0};
     }
-    MODA_TRACE(4);  // PV
-    wait_vmem();
-    MODA_TRACE(5);  // wait for this wave's loads
     __syncthreads();
-    MODA_TRACE(6);  // barrier
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // key tiles [0, n_nm) lie entirely at or before this wave's first token
-  const int n_nm = (int)min((int64_t)n_kt, (wave_tok_lo + 1) / NKEY);
-  int j = 0;
-  for (; j + 1 < n_nm; j += 2) {
-    body(j, I0{}, std::false_type{});
-    body(j + 1, I1{}, std::false_type{});
-  }
-  for (; j < n_kt; ++j) {
-    const bool mk = j >= n_nm;
-    if (j & 1) {
-      if (mk) body(j, I1{}, std::true_type{});
-      else body(j, I1{}, std::false_type{});
-    } else {
-      if (mk) body(j, I0{}, std::true_type{});
-      else body(j, I0{}, std::false_type{});
+#pragma unroll
+    for (int q = 0; q < 2 * DMA_INSTR; ++q) dma_one(q, 0, k_lds0, v_lds0);
+    wait_vmem();
+    __syncthreads();
+    MODA_TRACE(0);  // prologue
+
+    // iteration j with buffer parity P = j % 2: loads tile j+1 into the other
+    // buffers (last read in iteration j-1), computes tile j
+    auto body = [&](int j, auto parity, auto masked) {
+      constexpr int P = decltype(parity)::value;
+      const char *const k_rd = P ? k_lds1 : k_lds0;
+      const char *const v_rd = P ? v_lds1 : v_lds0;
+      char *const k_wr = P ? k_lds0 : k_lds1;
+      char *const v_wr = P ? v_lds0 : v_lds1;
+      MODA_TRACE(1);  // (loads are issued inside the QK^T sequence)
+      // S^T = K Q^T: the two 32-key chains alternate, K fragments are read four
+      // MFMAs ahead and the eight loads of tile j+1 are spread between the
+      // MFMAs; sched_barrier fences keep this order.
+      floatx16 s[2];
+      {
+        bf16x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = kfrag(k_rd, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ks = i >> 1, kb2 = i & 1;
+          const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], qb[ks], c, 0, 0, 0);
+          if (i + 4 < 16) a[i & 3] = kfrag(k_rd, i + 4);
+          if (i % (16 / (2 * DMA_INSTR)) == 0) dma_one(i / (16 / (2 * DMA_INSTR)), j + 1, k_wr, v_wr);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      MODA_TRACE(2);  // QK^T
+      if constexpr (decltype(masked)::value) mask(s, j);
+      bf16x8 pb[4];
+      softmax_update<2>(st, s, sc, pb);
+      MODA_TRACE(3);  // mask + softmax
+      // O^T += V^T P^T: V fragments (two transpose reads each) three MFMAs ahead
+      {
+        bf16x8 a[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, pv_order(i));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int f = pv_order(i);
+          st.acc[f >> 2] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[f & 3], st.acc[f >> 2], 0, 0, 0);
+          if (i + 3 < 16) a[i % 3] = vfrag(v_rd, pv_order(i + 3));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      MODA_TRACE(4);  // PV
+      wait_vmem();
+      MODA_TRACE(5);  // wait for this wave's loads
+      __syncthreads();
+      MODA_TRACE(6);  // barrier
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // key tiles [0, n_nm) lie entirely at or before this wave's first token
+    const int n_nm = (int)min((int64_t)n_kt, (wave_tok_lo + 1) / NKEY);
+    int j = 0;
+    for (; j + 1 < n_nm; j += 2) {
+      body(j, I0{}, std::false_type{});
+      body(j + 1, I1{}, std::false_type{});
+    }
+    for (; j < n_kt; ++j) {
+      const bool mk = j >= n_nm;
+      if (j & 1) {
+        if (mk) body(j, I1{}, std::true_type{});
+        else body(j, I1{}, std::false_type{});
+      } else {
+        if (mk) body(j, I0{}, std::true_type{});
+        else body(j, I0{}, std::false_type{});
+      }
     }
   }
 
@@ -603,7 +607,7 @@ __device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, int64_t i, flo
   p[i] = (uint16_t)float_to_bf16_bits(v);
 }
 
-template <typename E, int DG, bool HAS_DEPTH>
+template <typename E, int DG, bool HAS_DEPTH, bool HAS_SEQ>
 __global__ __launch_bounds__(64) void moda_fwd_generic(FwdArgs p) {
   __shared__ float qs[DG];
   __shared__ float red[64][DG + 1];
@@ -643,7 +647,8 @@ __global__ __launch_bounds__(64) void moda_fwd_generic(FwdArgs p) {
     for (int n = 0; n < DG; ++n) o[n] = fmaf(pw, load_elem(vr, n), o[n]);
   };
 
-  for (int64_t j = lane; j <= t; j += 64) visit(k + j * DG, v + j * DG);
+  if (HAS_SEQ)
+    for (int64_t j = lane; j <= t; j += 64) visit(k + j * DG, v + j * DG);
   if (HAS_DEPTH && p.L > 0) {
     const int64_t L = p.L;
     const int64_t half = p.B * p.Hkv * T * L * DG;  // elements of Kd
@@ -691,10 +696,15 @@ hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t TQ = M / G;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const int64_t grid = ntiles * a.B * a.Hkv;
-  if (a.has_depth)
-    hipLaunchKernelGGL((moda_fwd_mfma<true>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s, a);
+  if (!a.has_seq)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
+                       a);
+  else if (a.has_depth)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((moda_fwd_mfma<false>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
+                       a);
   return hipGetLastError();
 }
 
@@ -707,10 +717,15 @@ hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s) {
 template <typename E, int DG>
 static hipError_t launch_generic_d(const FwdArgs &a, hipStream_t s) {
   const int64_t rows = a.B * a.Hq * a.T;
-  if (a.has_depth)
-    hipLaunchKernelGGL((moda_fwd_generic<E, DG, true>), dim3((uint32_t)rows), dim3(64), 0, s, a);
+  if (!a.has_seq)
+    hipLaunchKernelGGL((moda_fwd_generic<E, DG, true, false>), dim3((uint32_t)rows), dim3(64), 0,
+                       s, a);
+  else if (a.has_depth)
+    hipLaunchKernelGGL((moda_fwd_generic<E, DG, true, true>), dim3((uint32_t)rows), dim3(64), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((moda_fwd_generic<E, DG, false>), dim3((uint32_t)rows), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_generic<E, DG, false, true>), dim3((uint32_t)rows), dim3(64), 0,
+                       s, a);
   return hipGetLastError();
 }
 

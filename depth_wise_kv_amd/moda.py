@@ -23,7 +23,8 @@ MODA_F32, MODA_BF16 = 0, 1
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
-           "moda_causal_fwd", "moda_status_string", "moda_last_error", "moda_fwd_variant")
+           "moda_causal_fwd", "moda_depth_fwd", "moda_status_string", "moda_last_error",
+           "moda_fwd_variant")
 
 
 class ModaShape(ctypes.Structure):
@@ -54,6 +55,8 @@ def _load():
     lib.moda_fwd.restype = ctypes.c_int
     lib.moda_causal_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp]
     lib.moda_causal_fwd.restype = ctypes.c_int
+    lib.moda_depth_fwd.argtypes = [sp, vp, vp, sz, vp, vp, vp]
+    lib.moda_depth_fwd.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     lib.moda_last_error.argtypes = []
@@ -110,6 +113,11 @@ def moda_fwd(shape, q_ptr, k_ptr, v_ptr, packed_ptr, packed_bytes, out_ptr, lse_
 
 def moda_causal_fwd(shape, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream):
     return lib.moda_causal_fwd(_sref(shape), q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream)
+
+
+def moda_depth_fwd(shape, q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr, stream):
+    return lib.moda_depth_fwd(_sref(shape), q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr,
+                              stream)
 
 
 def moda_status_string(status: int) -> str:
@@ -192,6 +200,32 @@ def causal_fwd(q, k, v, *, with_lse: bool = False, out=None, lse=None):
     _check(moda_causal_fwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                            _stream_ptr(q)), "moda_causal_fwd")
     return (out, lse) if with_lse else out
+
+
+def depth_fwd(q, packed, Hkv: int, L: int, *, with_lse: bool = False, out=None, lse=None):
+    """Depth attention alone over a packed depth cache (the same packed
+    buffer moda_fwd reads; Hkv and L are those of the pack shape)."""
+    import torch
+    _check_tensors(q, packed)
+    B, Hq, T, d = q.shape
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    nbytes = 0 if packed is None else packed.numel() * packed.element_size()
+    _check(moda_depth_fwd(shape, _ptr(q), _ptr(packed), nbytes, _ptr(out), _ptr(lse),
+                          _stream_ptr(q)), "moda_depth_fwd")
+    return (out, lse) if with_lse else out
+
+
+def depth_forward(q, kd, vd, *, with_lse: bool = False):
+    """Pack then depth attention alone."""
+    B, Hq, T, d = q.shape
+    Hkv, L = kd.shape[1], kd.shape[3]
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
+    packed = pack_depth_cache(kd, vd, shape)
+    return depth_fwd(q, packed, Hkv, L, with_lse=with_lse)
 
 
 def moda_forward(q, k, v, kd=None, vd=None, *, with_lse: bool = False):

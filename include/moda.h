@@ -110,6 +110,24 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k,
                             const void *v, void *out, float *lse,
                             void *hip_stream);
 
+/* Depth attention alone: each query row (b, h, t) attends over its own
+ * token's L depth entries only, under one softmax scaled by 1/sqrt(d), and
+ * gets their weighted values.  No sequence key takes part.
+ *
+ * Passage: hyper.ai page on arXiv 2603.15619, section "Depth stream
+ * mechanism" (the read step of the depth stream: attention over the keys and
+ * values that the preceding layers left at the same token position).
+ *
+ *   q      : Q [B, Hq, T, d] (read only)
+ *   packed : from moda_pack_depth_cache with the same shape (read only)
+ *   out    : O [B, Hq, T, d], written in full
+ *   lse    : NULL, or LSE [B, Hq, T] float32 over the depth logits alone
+ * Requires L >= 1 (an empty softmax has no value): MODA_ERR_INVALID_ARG
+ * otherwise.  Same validation, ownership and asynchrony as moda_fwd. */
+moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packed,
+                           size_t packed_bytes, void *out, float *lse,
+                           void *hip_stream);
+
 /* Static text of a status code (never NULL). */
 const char *moda_status_string(moda_status st);
 

@@ -92,6 +92,15 @@ def test_fwd_rejects_before_launch(m):
     assert m.moda_pack_depth_cache(s, p, p, p, nb - 16, None) == m.MODA_ERR_INVALID_ARG
     assert m.moda_pack_depth_cache(s0, p, p, p, 0, None) == m.MODA_ERR_INVALID_ARG
     assert m.moda_pack_depth_cache(s, p, None, p, nb, None) == m.MODA_ERR_INVALID_ARG
+    # depth attention alone: needs L >= 1, q, out and a large enough packed cache
+    assert m.moda_depth_fwd(s0, p, p, 16, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert "L >= 1" in m.moda_last_error()
+    assert m.moda_depth_fwd(s, None, p, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_depth_fwd(s, p, p, nb, None, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_depth_fwd(s, p, None, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_depth_fwd(s, p, p, nb - 1, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_depth_fwd(s, p, p, nb, mis, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_depth_fwd(None, p, p, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
 
 
 def test_binding_refuses_host_tensors(m):

@@ -169,6 +169,49 @@ def test_rescale_paths(m, dev, kind, Hq, Hkv):
     assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
 
 
+# ------------------------------------------------------------------ depth attention alone
+
+DEPTH_SHAPES = [  # (B, Hq, Hkv, T, L, d, dtype): MFMA path and generic path, ragged sizes
+    (1, 16, 4, 70, 5, 128, "bf16"), (2, 4, 4, 9, 33, 128, "bf16"), (1, 8, 1, 40, 65, 128, "bf16"),
+    (1, 32, 8, 300, 128, 128, "bf16"), (1, 2, 1, 64, 4, 32, "f32"), (1, 6, 2, 30, 3, 64, "bf16"),
+    (2, 4, 2, 17, 1, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L,d,dt", DEPTH_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}d{d}{dt}"
+                              for b, hq, hk, t, l, d, dt in DEPTH_SHAPES])
+def test_depth_only_parity(m, dev, B, Hq, Hkv, T, L, d, dt):
+    """moda_depth_fwd against the oracle's depth attention, every row."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, d=d, dtype=dt, seed=900 + T + L)
+    h_in, d_in = host_case(cfg, dev)
+    out, lse = m.depth_forward(d_in["q"], d_in["kd"], d_in["vd"], with_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.depth_forward(h_in["q"], h_in["kd"], h_in["vd"])
+    tol, ltol = (F32_TOL, LSE_TOL_F32) if dt == "f32" else (BF16_TOL, LSE_TOL_BF16)
+    e_o, e_l = max_err(out_to_f64(out), ref), max_err(lse.cpu().numpy(), rlse)
+    print(f"[parity] depth-only {cfg} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= tol and e_l <= ltol
+
+
+def test_depth_only_merges_with_causal(m, dev):
+    """GPU causal attention and GPU depth attention alone, merged through
+    their LSEs, reproduce the GPU MoDA forward (one softmax over the union)."""
+    cfg = shape_cfg(1, 16, 4, 600, 24, seed=77)
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, cfg["L"])
+    o_s, l_s = m.causal_fwd(d_in["q"], d_in["k"], d_in["v"], with_lse=True)
+    o_d, l_d = m.depth_forward(d_in["q"], d_in["kd"], d_in["vd"], with_lse=True)
+    l_s, l_d = l_s.double(), l_d.double()
+    mm = torch.maximum(l_s, l_d)
+    a, c = torch.exp(l_s - mm), torch.exp(l_d - mm)
+    merged = (a[..., None] * o_s.double() + c[..., None] * o_d.double()) / (a + c)[..., None]
+    e_o = (merged - out.double()).abs().max().item()
+    e_l = (mm + torch.log(a + c) - lse.double()).abs().max().item()
+    print(f"[parity] causal+depth merge max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_l0_equals_causal_bitwise(m, dev):
