@@ -62,6 +62,8 @@ def load(path: str | None = None):
     lib.oracle_moda_row_weights.restype = ctypes.c_int
     lib.oracle_depth_fwd.argtypes = [i64] * 6 + [ctypes.c_int] + [vp] * 3 + [dp, dp]
     lib.oracle_depth_fwd.restype = ctypes.c_int
+    lib.oracle_moda_bwd.argtypes = [i64] * 6 + [ctypes.c_int] + [vp] * 6 + [dp] * 5
+    lib.oracle_moda_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
@@ -191,6 +193,36 @@ def depth_forward(q, kd, vd, *, lib=None):
     if rc:
         raise ValueError(f"oracle_depth_fwd failed with code {rc}")
     return out, lse
+
+
+def moda_backward(q, k, v, kd, vd, dout, *, lib=None):
+    """fp64 MoDA backward: gradients of a loss whose gradient with respect to
+    the MoDA output is ``dout`` [B,Hq,T,d] (same element type as q).
+
+    Returns (dq [B,Hq,T,d], dk, dv [B,Hkv,T,d], dkd, dvd [B,Hkv,T,L,d] or None
+    when L = 0), all float64.
+    """
+    lib = lib or load()
+    code = _code_of(q)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    L = 0 if kd is None else kd.shape[3]
+    q, k, v, dout = (_as_input(x, code) for x in (q, k, v, dout))
+    if L:
+        kd, vd = _as_input(kd, code), _as_input(vd, code)
+    else:
+        kd = vd = None
+    dq = np.empty((B, Hq, T, d), np.float64)
+    dk = np.empty((B, Hkv, T, d), np.float64)
+    dv = np.empty((B, Hkv, T, d), np.float64)
+    dkd = np.empty((B, Hkv, T, L, d), np.float64) if L else None
+    dvd = np.empty((B, Hkv, T, L, d), np.float64) if L else None
+    rc = lib.oracle_moda_bwd(B, Hq, Hkv, T, L, d, code, _ptr(q), _ptr(k), _ptr(v), _ptr(kd),
+                             _ptr(vd), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
+                             _ptr(dvd))
+    if rc:
+        raise ValueError(f"oracle_moda_bwd failed with code {rc}")
+    return dq, dk, dv, dkd, dvd
 
 
 def num_threads(*, lib=None) -> int:

@@ -284,3 +284,85 @@ int oracle_depth_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t L,
   }
   return failed ? 2 : 0;
 }
+
+/*
+ * MoDA backward: gradients of a scalar loss through the forward above, given
+ * the loss's gradient dO with respect to the output.  Calculus on the plain
+ * definition (the forward's steps 1-6), one query row at a time:
+ *   7. recompute the explicit list x, the weights p and o_t as in steps 1-5
+ *   8. D = <dO_t, o_t>
+ *   9. dp_n = <dO_t, value_n>   for every entry n of the list
+ *  10. ds_n = p_n * (dp_n - D)  (gradient through the softmax)
+ *  11. dq_t      = s * sum_n ds_n key_n
+ *      dK_j     += s * ds_j q_t ;  dV_j     += p_j dO_t          (j = 0..t)
+ *      dKd_{t,i}+= s * ds_{t+1+i} q_t ; dVd_{t,i} += p_{t+1+i} dO_t
+ * The sums over query rows run over every row that reads the entry: the G
+ * query heads of the KV group and, for sequence keys, every token t >= j.
+ *   dout [B,Hq,T,d] in the input element type
+ *   dq [B,Hq,T,d]; dk, dv [B,Hkv,T,d]; dkd, dvd [B,Hkv,T,L,d] (NULL if L == 0),
+ *   all double, fully written.
+ * Returns 0 on success, nonzero on a bad shape or an allocation failure.
+ */
+int oracle_moda_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t L,
+                    int64_t d, int dtype, const void *q, const void *k,
+                    const void *v, const void *kd, const void *vd,
+                    const void *dout, double *dq, double *dk, double *dv,
+                    double *dkd, double *dvd) {
+  if (bad_shape(B, Hq, Hkv, T, L, d, dtype)) return 1;
+  const int64_t G = Hq / Hkv;
+  const double s = 1.0 / sqrt((double)d);
+  memset(dk, 0, (size_t)(B * Hkv * T * d) * sizeof(double));
+  memset(dv, 0, (size_t)(B * Hkv * T * d) * sizeof(double));
+  if (L > 0) {
+    memset(dkd, 0, (size_t)(B * Hkv * T * L * d) * sizeof(double));
+    memset(dvd, 0, (size_t)(B * Hkv * T * L * d) * sizeof(double));
+  }
+  int fail = 0;
+  /* one (b, kv head) per iteration: it owns its dK, dV, dKd, dVd */
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)(T + L) * sizeof(double));
+    double *o = (double *)malloc((size_t)d * sizeof(double));
+    if (!x || !o) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+        const int64_t kv_off = bg * T * d;
+        for (int64_t h = (bg % Hkv) * G; h < (bg % Hkv + 1) * G; ++h) {
+          for (int64_t t = 0; t < T; ++t) {
+            const int64_t r = ((bg / Hkv) * Hq + h) * T + t; /* query row */
+            const int64_t dep_off = (bg * T + t) * L * d;
+            const int64_t n = t + 1 + L;
+            /* step 7: weights p (in x) and o_t, as in the forward */
+            moda_row(t, L, d, dtype, q, r * d, k, v, kv_off, kd, vd, dep_off, o, NULL, x, NULL);
+            /* step 8 */
+            double D = 0.0;
+            for (int64_t c = 0; c < d; ++c) D += elem(dout, r * d + c, dtype) * o[c];
+            for (int64_t c = 0; c < d; ++c) dq[r * d + c] = 0.0;
+            for (int64_t nn = 0; nn < n; ++nn) {
+              const int is_seq = nn <= t;
+              const void *key = is_seq ? k : kd, *val = is_seq ? v : vd;
+              const int64_t off = is_seq ? kv_off + nn * d : dep_off + (nn - t - 1) * d;
+              /* steps 9 and 10 */
+              const double dp = dot(dout, r * d, val, off, d, dtype);
+              const double ds = x[nn] * (dp - D);
+              /* step 11 */
+              double *dkey = is_seq ? dk + off : dkd + off;
+              double *dval = is_seq ? dv + off : dvd + off;
+              for (int64_t c = 0; c < d; ++c) {
+                dq[r * d + c] += s * ds * elem(key, off + c, dtype);
+                dkey[c] += s * ds * elem(q, r * d + c, dtype);
+                dval[c] += x[nn] * elem(dout, r * d + c, dtype);
+              }
+            }
+          }
+        }
+      }
+    }
+    free(x);
+    free(o);
+  }
+  return fail ? 2 : 0;
+}

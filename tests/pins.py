@@ -19,6 +19,9 @@ Sources of the facts:
   * same page, section "Depth stream mechanism": depth attention alone reads
     the token's own depth entries under one softmax.  -> pins o to s (the
     oracle's standalone depth attention)
+  * the backward is calculus on the forward: central finite differences of
+    the (pinned) forward oracle and PyTorch autograd through an independent
+    fp64 formulation.  -> pins t to w
 """
 from __future__ import annotations
 
@@ -380,6 +383,93 @@ def pin_s_depth_dominance(lib):
     out, lse = _depth(lib, q, kd, vd)
     _close(out[0, 0], vd[0, 0, :, 1], tol=1e-12, what="depth dominance")
     _close(lse[0, 0], np.full(T, 1000.0), tol=1e-9, what="depth dominance lse")
+
+
+def _bwd_case(B, Hq, Hkv, T, L, d, seed):
+    q, k, v, kd, vd = _case(B, Hq, Hkv, T, L, d, seed)
+    dout = np.random.default_rng(seed + 1).standard_normal(q.shape)
+    return q, k, v, kd, vd, dout
+
+
+def _bwd(lib, q, k, v, kd, vd, dout):
+    if kd is not None and kd.shape[3] == 0:
+        kd = vd = None
+    return oracle.moda_backward(q, k, v, kd, vd, dout, lib=lib)
+
+
+def pin_t_bwd_finite_differences(lib):
+    """Each gradient matches the central difference of the forward oracle's
+    loss sum(dO * O) along a random direction (step 1e-5: error ~1e-10)."""
+    for (B, Hq, Hkv, T, L, d, seed) in [(1, 4, 2, 5, 3, 4, 171), (2, 2, 2, 3, 0, 8, 172),
+                                        (1, 4, 1, 1, 4, 3, 173), (1, 8, 2, 6, 2, 5, 174)]:
+        q, k, v, kd, vd, dout = _bwd_case(B, Hq, Hkv, T, L, d, seed)
+        grads = _bwd(lib, q, k, v, kd, vd, dout)
+        xs = [q, k, v, kd, vd]
+        rng = np.random.default_rng(seed + 2)
+
+        def loss(args):
+            o, _ = _fwd(lib, *args)
+            return float((o * dout).sum())
+
+        for i in range(5 if L else 3):
+            u = rng.standard_normal(xs[i].shape)
+            eps = 1e-5
+            xp, xm = list(xs), list(xs)
+            xp[i], xm[i] = xs[i] + eps * u, xs[i] - eps * u
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            an = float((grads[i] * u).sum())
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), \
+                f"finite difference of input {i} {B,Hq,Hkv,T,L,d}: {fd} vs {an}"
+
+
+def pin_u_bwd_autograd(lib):
+    """Gradients agree with PyTorch autograd (fp64, CPU) through the
+    concatenate-then-softmax formulation written with torch ops."""
+    import torch
+    for (B, Hq, Hkv, T, L, d, seed) in [(1, 4, 2, 7, 3, 8, 181), (2, 2, 1, 5, 1, 4, 182),
+                                        (1, 2, 2, 6, 0, 8, 183)]:
+        q, k, v, kd, vd, dout = _bwd_case(B, Hq, Hkv, T, L, d, seed)
+        tq, tk, tv, tkd, tvd = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                                for x in (q, k, v, kd, vd))
+        G = Hq // Hkv
+        ke, ve = tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1)
+        sc = torch.matmul(tq, ke.transpose(-1, -2)) / math.sqrt(d)
+        sc = sc.masked_fill(torch.triu(torch.ones(T, T, dtype=torch.bool), 1), float("-inf"))
+        if L:
+            kde, vde = tkd.repeat_interleave(G, 1), tvd.repeat_interleave(G, 1)
+            sd = torch.einsum("bhtd,bhtld->bhtl", tq, kde) / math.sqrt(d)
+            p = torch.softmax(torch.cat([sc, sd], -1), -1)
+            o = torch.matmul(p[..., :T], ve) + torch.einsum("bhtl,bhtld->bhtd", p[..., T:], vde)
+        else:
+            o = torch.matmul(torch.softmax(sc, -1), ve)
+        (o * torch.tensor(dout)).sum().backward()
+        got = _bwd(lib, q, k, v, kd, vd, dout)
+        for name, g, t in zip("q k v kd vd".split(), got, (tq, tk, tv, tkd, tvd)):
+            if g is None:
+                continue
+            _close(g, t.grad.numpy(), tol=1e-10, what=f"autograd d{name} {B,Hq,Hkv,T,L,d}")
+
+
+def pin_v_bwd_zero_upstream(lib):
+    """dO = 0 gives exactly zero gradients."""
+    q, k, v, kd, vd, dout = _bwd_case(1, 4, 2, 6, 3, 8, 191)
+    for g in _bwd(lib, q, k, v, kd, vd, np.zeros_like(dout)):
+        assert not np.any(g), "nonzero gradient from a zero upstream gradient"
+
+
+def pin_w_bwd_input_decoding(lib):
+    """fp32 and bf16 inputs (dO included) are read exactly by the backward."""
+    q, k, v, kd, vd, dout = _bwd_case(1, 2, 1, 5, 2, 8, 201)
+    xs = [x.astype(np.float32) for x in (q, k, v, kd, vd, dout)]
+    g32 = _bwd(lib, *xs)
+    g64 = _bwd(lib, *(x.astype(np.float64) for x in xs))
+    for a, b in zip(g32, g64):
+        assert np.array_equal(a, b), "fp32 decoding in the backward"
+    xb = [f32_to_bf16_bits(x) for x in xs]
+    gb = _bwd(lib, *xb)
+    gb64 = _bwd(lib, *(bf16_bits_to_f32(x).astype(np.float64) for x in xb))
+    for a, b in zip(gb, gb64):
+        assert np.array_equal(a, b), "bf16 decoding in the backward"
 
 
 PINS = [(name, fn) for name, fn in sorted(globals().items()) if name.startswith("pin_")]

@@ -45,6 +45,16 @@ MUTANTS = [
     ("depth_only_lse_no_max", "if (lse) lse[r] = mx + log(Zd);", "if (lse) lse[r] = log(Zd);",
      1),
     ("depth_only_unnormalised", "acc += (c[i] / Zd) *", "acc += c[i] *", 1),
+    # backward
+    ("bwd_no_D", "const double ds = x[nn] * (dp - D);", "const double ds = x[nn] * dp;", 1),
+    ("bwd_dq_no_scale", "dq[r * d + c] += s * ds *", "dq[r * d + c] += ds *", 1),
+    ("bwd_dkey_no_scale", "dkey[c] += s * ds *", "dkey[c] += ds *", 1),
+    ("bwd_dval_from_ds", "dval[c] += x[nn] *", "dval[c] += ds *", 1),
+    ("bwd_group_head0", "h < (bg % Hkv + 1) * G; ++h)", "h < (bg % Hkv) * G + 1; ++h)", 1),
+    ("bwd_depth_prev_token", "const int64_t dep_off = (bg * T + t) * L * d;",
+     "const int64_t dep_off = (bg * T + (t > 0 ? t - 1 : 0)) * L * d;", 1),
+    ("bwd_D_from_dout_only", "D += elem(dout, r * d + c, dtype) * o[c];",
+     "D += elem(dout, r * d + c, dtype);", 1),
 ]
 
 
