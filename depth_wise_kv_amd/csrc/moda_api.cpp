@@ -233,6 +233,53 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
   return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "depth launch");
 }
 
+moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const void *v,
+                     const void *k_depth, const void *v_depth, const void *packed,
+                     size_t packed_bytes, const void *out, const float *lse, const void *dout,
+                     void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth, float *delta,
+                     void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (!use_mfma(s)) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports bf16 with d = 128");
+  if (s->Hq / s->Hkv > 64) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports G up to 64");
+  if (s->L > 0) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd: depth gradients not built yet");
+  st = check_qkvo(q, k, v, out, lse);
+  if (st != MODA_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv || !delta)
+    return fail(MODA_ERR_INVALID_ARG, "lse, dout, dq, dk, dv and delta must be non-NULL");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(delta))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (s->L == 0 && (k_depth || v_depth || packed || packed_bytes || dk_depth || dv_depth))
+    return fail(MODA_ERR_INVALID_ARG, "depth arguments must be NULL when L == 0");
+  moda::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.packed = packed;
+  a.kd = k_depth;
+  a.vd = v_depth;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dkd = dk_depth;
+  a.dvd = dv_depth;
+  a.B = s->B;
+  a.Hq = s->Hq;
+  a.Hkv = s->Hkv;
+  a.T = s->T;
+  a.L = s->L;
+  a.d = s->d;
+  a.nblk = depth_blocks(s);
+  a.scale = (float)(1.0 / std::sqrt((double)s->d));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
+  return hip_status(moda::launch_bwd(a, (hipStream_t)hip_stream), "bwd launch");
+}
+
 const char *moda_status_string(moda_status st) {
   switch (st) {
     case MODA_OK: return "MODA_OK";

@@ -1,0 +1,582 @@
+// HIP kernels of the MoDA backward for gfx950 (MI355X): bf16, head dim 128.
+//
+// Given dO, the loss gradient with respect to the MoDA output O, and the
+// forward's per-row log-sum-exp, the gradients follow from the chain rule
+// through the one softmax over sequence and depth entries (hyper.ai page on
+// arXiv 2603.15619, section "Mixture-of-Depths Attention (MoDA)"):
+//   p_n = exp(s <q, key_n> - lse)           (the forward's weights)
+//   D   = <dO, O>                            per query row
+//   ds_n = p_n (<dO, value_n> - D)
+//   dQ  = s sum_n ds_n key_n;  dKey_n += s ds_n q;  dValue_n += p_n dO
+// with s = 1/sqrt(d).  Sums over query rows run over every row that reads
+// the entry: the G query heads of the KV group, and for a sequence key j
+// every token t >= j.
+//
+// Kernels:
+//   moda_bwd_delta  D for every query row.
+//   moda_bwd_dq     dQ.  A workgroup owns 256 query rows (the forward's
+//                   tiling: 256/G tokens x the G heads of one KV group) and
+//                   walks the key tiles up to the diagonal.  Per tile:
+//                   S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T,
+//                   all on v_mfma_f32_32x32x16_bf16 with a lane owning a row.
+//   moda_bwd_dkdv   dK, dV.  A workgroup owns 128 sequence keys (4 waves x 32)
+//                   and walks the query tiles of 64 rows (64/G tokens x G
+//                   heads) from its first key to the end.  Per tile and
+//                   32-row block: S = Q K^T, P, dP = dO V^T, dS,
+//                   dV^T += dO^T P, dK^T += Q^T dS, with a lane owning a key.
+// The key and query tiles go from global memory straight into LDS.  Each
+// tile is stored twice where it is read both ways: "row-swizzled" (chunk c
+// of row r in slot c ^ (r % 16), for operands that hold 8 dims of one row)
+// and "column-swizzled" (chunk c in slot c ^ 4 (r % 4), for transpose reads
+// that hold 4 rows of one dim).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "moda_device.h"
+#include "moda_internal.h"
+
+namespace moda {
+namespace {
+
+constexpr int BD = kMfmaD;                 // 128
+constexpr int BTILE = 64 * BD * 2;         // 16 KiB: 64 rows of 256 B
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Per-lane LDS addressing for a 64-row tile of 256-byte rows.
+//   rowfrag(buf, i): A or B operand holding row 32*(i & 1) + lane%32, dims
+//                    64*(lane/32) + 8*(i >> 1) .. +7 (row-swizzled tile)
+//   colfrag(buf, i): A operand of a transposed product, i = 4*nb + kk: dims
+//                    32*nb + lane%32, the 8 rows of k-step kk that pair with
+//                    the register order of an MFMA result (column-swizzled)
+struct TileFrags {
+  int k_row, k_x;
+  int vaddr[4];
+  __device__ explicit TileFrags(int lane) {
+    const int li = lane & 31, lh = lane >> 5;
+    k_row = li * 256 + 16 * ((8 * lh) ^ (li & 8));
+    k_x = li & 7;
+    const int lg = lane >> 4, lq = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      vaddr[nb] = (4 * (lg >> 1) + (lq >> 2)) * 256 +
+                  16 * (4 * (nb ^ (lq >> 2)) + 2 * (lg & 1) + ((lq & 3) >> 1)) + 8 * (lq & 1);
+  }
+  __device__ bf16x8 rowfrag(const char *b, int i) const {
+    return *(const bf16x8 *)(b + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
+  }
+  __device__ bf16x8 colfrag(const char *b, int i) const {
+    const char *vp = b + vaddr[i >> 2] + 16 * (i & 3) * 256;
+    const shortx4 lo = lds_read_tr(vp);
+    const shortx4 hi = lds_read_tr(vp + 8 * 256);
+    return __builtin_bit_cast(
+        bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+  }
+};
+
+// 16-byte chunk that LDS slot `slot` of tile row `row` holds
+__device__ __forceinline__ int row_swz(int row, int slot) { return slot ^ (row & 15); }
+__device__ __forceinline__ int col_swz(int row, int slot) { return slot ^ (4 * (row & 3)); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char *lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds,
+                                           16, voff, soff, 0, 0);
+}
+
+// Row r of a 256-B-row bf16 matrix into the B (or A) operand layout used for
+// Q in the forward: lane half h holds dims 64h .. 64h+63, 8 per k-step.
+__device__ __forceinline__ void load_row_operand(const __bf16 *row, bool ok, int lh,
+                                                 bf16x8 (&dst)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 u = ok ? *(const u32x4 *)(row + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+    dst[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+// Store an MFMA accumulator of a 128-dim row (column lane%32, registers over
+// dims 32*nb + 8*(r/4) + 4*(lane/32) + r%4) as bf16, scaled.
+__device__ __forceinline__ void store_row(__bf16 *row, const floatx16 (&acc)[4], float scale,
+                                          int lh) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 o;
+      o[0] = cvt_bf16x2(acc[nb][4 * g + 0] * scale, acc[nb][4 * g + 1] * scale);
+      o[1] = cvt_bf16x2(acc[nb][4 * g + 2] * scale, acc[nb][4 * g + 3] * scale);
+      *(u32x2 *)(row + 32 * nb + 8 * g + 4 * lh) = o;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// D = <dO, O> per query row (fp32), one thread per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void moda_bwd_delta(BwdArgs p) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.B * p.Hq * p.T) return;
+  const u32x4 *o = (const u32x4 *)((const __bf16 *)p.out + r * BD);
+  const u32x4 *g = (const u32x4 *)((const __bf16 *)p.dout + r * BD);
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < BD / 8; ++c) {
+    const u32x4 a = o[c], b = g[c];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(bf16_bits_to_float(a[w] & 0xFFFFu), bf16_bits_to_float(b[w] & 0xFFFFu), acc);
+      acc = fmaf(bf16_bits_to_float(a[w] >> 16), bf16_bits_to_float(b[w] >> 16), acc);
+    }
+  }
+  p.delta[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 8 waves x 32 query rows, key tiles of 64.
+// ---------------------------------------------------------------------------
+constexpr int DQ_WAVES = 8;
+constexpr int DQ_ROWS = 32 * DQ_WAVES;  // 256
+
+__global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
+  const int G = (int)(p.Hq / p.Hkv);
+  const int TQ = DQ_ROWS / G;
+  __shared__ __attribute__((aligned(1024))) char kn0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char kn1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char kt0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char vn0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char vn1[BTILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5;
+  const TileFrags fr(lane);
+
+  const int64_t T = p.T;
+  const int64_t BH = p.B * p.Hkv;
+  const int64_t ntiles = (T + TQ - 1) / TQ;
+  const int64_t x = blockIdx.x;
+  const int64_t tile = ntiles - 1 - x / BH;  // heaviest causal tiles first
+  const int64_t bh = x % BH;
+  const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int64_t t0 = tile * TQ;
+
+  const int r = wave * 32 + li;
+  const bool row_used = r < TQ * G;
+  const int64_t tok = row_used ? t0 + r / G : T;
+  const int64_t head = hkv * G + (row_used ? r % G : 0);
+  const bool row_ok = tok < T;
+  const int64_t qrow = (b * p.Hq + head) * T + (row_ok ? tok : 0);
+
+  bf16x8 qb[8], gb[8];
+  load_row_operand((const __bf16 *)p.q + qrow * BD, row_ok, lh, qb);
+  load_row_operand((const __bf16 *)p.dout + qrow * BD, row_ok, lh, gb);
+  const float c = p.scale_log2;
+  // S^T starts at -lse2/c, dP^T at -D: then P = exp2(c * S^T) and dS = P dP^T
+  const float init_s = row_ok ? -(p.lse[qrow] * LOG2E) / c : -INFINITY;
+  const float init_dp = row_ok ? -p.delta[qrow] : 0.f;
+
+  floatx16 dq[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) dq[nb][rr] = 0.f;
+
+  const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
+  const int n_kt = (int)((tok_end + 63) / 64);
+  const int64_t wave_tok_lo = t0 + (wave * 32) / G;
+
+  // Tile loads: this wave fills tile rows 8*wave .. +7 of K (twice: row- and
+  // column-swizzled) and V (row-swizzled); 2 instructions of 4 rows each per
+  // copy.  Rows at or past T read as zeros (descriptor range).
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.k + bh * T * (BD * 2)), (short)0, (int)(T * (BD * 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.v + bh * T * (BD * 2)), (short)0, (int)(T * (BD * 2)), 0x00020000);
+  uint32_t off_r[2], off_c[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * wave + 4 * i + (lane >> 4);
+    off_r[i] = (uint32_t)(row * 256 + 16 * row_swz(row, lane & 15));
+    off_c[i] = (uint32_t)(row * 256 + 16 * col_swz(row, lane & 15));
+  }
+  // load q = 0..5 of tile kt: K row-swizzled, K column-swizzled, V row-swizzled
+  auto dma_one = [&](int qi, int kt, char *kn, char *ktr, char *vn) {
+    const uint32_t soff = (uint32_t)kt * BTILE;
+    const int i = qi & 1;
+    char *dst = (qi < 2 ? kn : qi < 4 ? ktr : vn) + (8 * wave + 4 * i) * 256;
+    if (qi < 2) dma16(k_rsrc, dst, off_r[i], soff);
+    else if (qi < 4) dma16(k_rsrc, dst, off_c[i], soff);
+    else dma16(v_rsrc, dst, off_r[i], soff);
+  };
+  // causal mask of key half kb2 of tile kt: register rr holds key
+  // 64*kt + 32*kb2 + 8*(rr/4) + 4*lh + rr%4
+  auto mask_half = [&](floatx16 &s, int kt, int kb2) {
+    const int lim = (int)max((int64_t)-8, min((int64_t)64, tok - (int64_t)kt * 64 - 4 * lh));
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[rr] = -INFINITY;
+  };
+
+  for (int o = tid * 16; o < BTILE; o += 64 * DQ_WAVES * 16) {
+    *(u32x4 *)(kn0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(kn1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(kt0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(kt1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(vn0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(vn1 + o) = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qi = 0; qi < 6; ++qi) dma_one(qi, 0, kn0, kt0, vn0);
+  wait_vmem();
+  __syncthreads();
+
+  auto body = [&](int j, auto parity, auto masked) {
+    constexpr int P = decltype(parity)::value;
+    const char *const kn_rd = P ? kn1 : kn0;
+    const char *const kt_rd = P ? kt1 : kt0;
+    const char *const vn_rd = P ? vn1 : vn0;
+    char *const kn_wr = P ? kn0 : kn1;
+    char *const kt_wr = P ? kt0 : kt1;
+    char *const vn_wr = P ? vn0 : vn1;
+    // The tile is taken as two halves of 32 keys (kb2), which keeps one
+    // half's scores, dP and dS in registers at a time.  The loads of tile
+    // j+1 are spread between the first half's MFMAs.
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      // S^T = K Q^T (from -lse2/c) for keys 32*kb2 .. +31
+      floatx16 s;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[rr] = init_s;
+      {
+        bf16x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = fr.rowfrag(kn_rd, 2 * i + kb2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 3], qb[ks], s, 0, 0, 0);
+          if (ks + 4 < 8) a[ks & 3] = fr.rowfrag(kn_rd, 2 * (ks + 4) + kb2);
+          if (kb2 == 0 && ks < 6) dma_one(ks, j + 1, kn_wr, kt_wr, vn_wr);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (decltype(masked)::value) mask_half(s, j, kb2);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
+      // dP^T = V dO^T (from -D)
+      floatx16 dp;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) dp[rr] = init_dp;
+      {
+        bf16x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = fr.rowfrag(vn_rd, 2 * i + kb2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 3], gb[ks], dp, 0, 0, 0);
+          if (ks + 4 < 8) a[ks & 3] = fr.rowfrag(vn_rd, 2 * (ks + 4) + kb2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // dS^T = P^T (dP^T - D) as bf16 B operands of k-steps 2*kb2, 2*kb2 + 1
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 8 * kk + 2 * q;
+          w[q] = cvt_bf16x2(s[rr] * dp[rr], s[rr + 1] * dp[rr + 1]);
+        }
+        dsb[kk] = __builtin_bit_cast(bf16x8, w);
+      }
+      // dQ^T += K^T dS^T over these 32 keys
+      {
+        bf16x8 a[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) a[i] = fr.colfrag(kt_rd, 4 * (i & 3) + 2 * kb2 + (i >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int nb = i & 3, kk = i >> 2;
+          dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], dsb[kk], dq[nb], 0, 0, 0);
+          if (i + 3 < 8)
+            a[i % 3] = fr.colfrag(kt_rd, 4 * ((i + 3) & 3) + 2 * kb2 + ((i + 3) >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  const int n_nm = (int)min((int64_t)n_kt, (wave_tok_lo + 1) / 64);
+  int j = 0;
+  for (; j + 1 < n_nm; j += 2) {
+    body(j, I0{}, std::false_type{});
+    body(j + 1, I1{}, std::false_type{});
+  }
+  for (; j < n_kt; ++j) {
+    const bool mk = j >= n_nm;
+    if (j & 1) {
+      if (mk) body(j, I1{}, std::true_type{});
+      else body(j, I1{}, std::false_type{});
+    } else {
+      if (mk) body(j, I0{}, std::true_type{});
+      else body(j, I0{}, std::false_type{});
+    }
+  }
+
+  if (row_ok) store_row((__bf16 *)p.dq + qrow * BD, dq, p.scale, lh);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves x 32 sequence keys, query tiles of 64 rows.
+// ---------------------------------------------------------------------------
+constexpr int KV_WAVES = 4;
+constexpr int KV_KEYS = 32 * KV_WAVES;  // 128
+constexpr int QROWS = 64;
+
+__global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
+  const int G = (int)(p.Hq / p.Hkv);
+  const int TQr = QROWS / G;  // tokens per query tile (G <= 64)
+  __shared__ __attribute__((aligned(1024))) char qn0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char qn1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char qt0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char qt1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char gn0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char gn1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char gt0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char gt1[BTILE];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];
+  __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5;
+  const TileFrags fr(lane);
+
+  const int64_t T = p.T;
+  const int64_t BH = p.B * p.Hkv;
+  const int64_t x = blockIdx.x;
+  const int64_t ktile = x / BH;  // key tile 0 (the heaviest) first
+  const int64_t bh = x % BH;
+  const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int64_t k0 = ktile * KV_KEYS;
+
+  // this lane's key (the column of every product) and its K, V rows as B operands
+  const int64_t key = k0 + 32 * wave + li;
+  const bool key_ok = key < T;
+  bf16x8 kb[8], vb[8];
+  load_row_operand((const __bf16 *)p.k + (bh * T + (key_ok ? key : 0)) * BD, key_ok, lh, kb);
+  load_row_operand((const __bf16 *)p.v + (bh * T + (key_ok ? key : 0)) * BD, key_ok, lh, vb);
+
+  floatx16 dk[4], dv[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) dk[nb][rr] = dv[nb][rr] = 0.f;
+
+  const float c = p.scale_log2;
+  const float neg_inv_c = -1.0f / c;
+  // query tiles: tokens from k0 (the first that sees a key of this workgroup)
+  const int64_t n_qt = (T - k0 + TQr - 1) / TQr;
+
+  // Tile loads.  Tile row r holds token t0 + r / G of head hkv*G + r % G; this
+  // wave loads rows 16*wave .. +15 of Q and of dO, each twice (row- and
+  // column-swizzled): 4 instructions of 4 rows per copy.  Rows past the
+  // tile's tokens point outside the descriptor range and read as zeros.
+  const int64_t grp = b * p.Hq + hkv * G;  // first query head row block of the group
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.q + grp * T * (BD * 2)), (short)0, (int)(G * T * (BD * 2)),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.dout + grp * T * (BD * 2)), (short)0, (int)(G * T * (BD * 2)),
+      0x00020000);
+  uint32_t off_r[4], off_c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + (lane >> 4);
+    const bool used = row < TQr * G;
+    const uint32_t base = (uint32_t)(((row % G) * T + row / G) * 256);
+    off_r[i] = used ? base + 16 * row_swz(row, lane & 15) : 0x80000000u;
+    off_c[i] = used ? base + 16 * col_swz(row, lane & 15) : 0x80000000u;
+  }
+  auto dma_tile = [&](int64_t qt, char *qn, char *qtr, char *gn, char *gtr) {
+    const uint32_t soff = (uint32_t)((k0 + qt * TQr) * 256);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lrow = (16 * wave + 4 * i) * 256;
+      dma16(q_rsrc, qn + lrow, off_r[i], soff);
+      dma16(q_rsrc, qtr + lrow, off_c[i], soff);
+      dma16(g_rsrc, gn + lrow, off_r[i], soff);
+      dma16(g_rsrc, gtr + lrow, off_c[i], soff);
+    }
+  };
+  // lse2 and D of tile row `lane` (wave 0 only): rows outside the problem get
+  // lse2 = +inf (weight 0) and D = 0
+  auto row_stats = [&](int64_t qt, float &l2, float &dl) {
+    const int row = lane;
+    const int64_t tk = k0 + qt * TQr + row / G;
+    if (row < TQr * G && tk < T) {
+      const int64_t qr = (grp + row % G) * T + tk;
+      l2 = p.lse[qr] * LOG2E;
+      dl = p.delta[qr];
+    } else {
+      l2 = INFINITY;
+      dl = 0.f;
+    }
+  };
+
+  for (int o = tid * 16; o < BTILE; o += 64 * KV_WAVES * 16) {
+    *(u32x4 *)(qn0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(qn1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(qt0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(qt1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(gn0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(gn1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(gt0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(gt1 + o) = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+  dma_tile(0, qn0, qt0, gn0, gt0);
+  if (wave == 0) {
+    float l2, dl;
+    row_stats(0, l2, dl);
+    lse_s[0][lane] = l2;
+    del_s[0][lane] = dl;
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // query tile qt in buffers of parity P; loads of tile qt+1 are issued first
+  auto body = [&](int64_t qt, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const char *const qn = P ? qn1 : qn0;
+    const char *const qtr = P ? qt1 : qt0;
+    const char *const gn = P ? gn1 : gn0;
+    const char *const gtr = P ? gt1 : gt0;
+    float l2n = 0.f, dln = 0.f;
+    const bool more = qt + 1 < n_qt;
+    if (more) {
+      dma_tile(qt + 1, P ? qn0 : qn1, P ? qt0 : qt1, P ? gn0 : gn1, P ? gt0 : gt1);
+      if (wave == 0) row_stats(qt + 1, l2n, dln);
+    }
+    const int64_t tq0 = k0 + qt * TQr;  // first token of the tile
+    // the tile needs the causal mask unless its first token is at or past
+    // this wave's last key
+    const bool masked = tq0 < k0 + 32 * wave + 31;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      // register rr of a 32-row block holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4
+      floatx16 s, dpv;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = 32 * sb + 8 * g + 4 * lh;
+        const float4 l4 = *(const float4 *)&lse_s[P][row0];
+        const float4 d4 = *(const float4 *)&del_s[P][row0];
+        s[4 * g + 0] = l4.x * neg_inv_c;
+        s[4 * g + 1] = l4.y * neg_inv_c;
+        s[4 * g + 2] = l4.z * neg_inv_c;
+        s[4 * g + 3] = l4.w * neg_inv_c;
+        dpv[4 * g + 0] = -d4.x;
+        dpv[4 * g + 1] = -d4.y;
+        dpv[4 * g + 2] = -d4.z;
+        dpv[4 * g + 3] = -d4.w;
+      }
+      // S = Q K^T (rows x keys)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(qn, 2 * ks + sb), kb[ks], s, 0, 0,
+                                                    0);
+      if (masked) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int row = 32 * sb + 8 * (rr >> 2) + 4 * lh + (rr & 3);
+          const int64_t tk = tq0 + (int64_t)((row + 0.5f) * (1.0f / (float)G));
+          if (tk < key) s[rr] = -INFINITY;
+        }
+      }
+      // P as fp32 and as bf16 B operands (k-step kk holds registers 8kk .. 8kk+7)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
+      bf16x8 pb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = cvt_bf16x2(s[8 * kk + 2 * q], s[8 * kk + 2 * q + 1]);
+        pb[kk] = __builtin_bit_cast(bf16x8, w);
+      }
+      // dP = dO V^T - D
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(gn, 2 * ks + sb), vb[ks], dpv, 0,
+                                                      0, 0);
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 8 * kk + 2 * q;
+          w[q] = cvt_bf16x2(s[rr] * dpv[rr], s[rr + 1] * dpv[rr + 1]);
+        }
+        dsb[kk] = __builtin_bit_cast(bf16x8, w);
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS  (k-steps 2*sb + kk of the tile)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(gtr, 4 * nb + 2 * sb + kk),
+                                                           pb[kk], dv[nb], 0, 0, 0);
+          dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(qtr, 4 * nb + 2 * sb + kk),
+                                                           dsb[kk], dk[nb], 0, 0, 0);
+        }
+    }
+    wait_vmem();
+    if (more && wave == 0) {
+      lse_s[P ^ 1][lane] = l2n;
+      del_s[P ^ 1][lane] = dln;
+    }
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int64_t qt = 0;
+  for (; qt + 1 < n_qt; qt += 2) {
+    body(qt, I0{});
+    body(qt + 1, I1{});
+  }
+  if (qt < n_qt) body(qt, I0{});
+
+  if (key_ok) {
+    store_row((__bf16 *)p.dk + (bh * T + key) * BD, dk, p.scale, lh);
+    store_row((__bf16 *)p.dv + (bh * T + key) * BD, dv, 1.0f, lh);
+  }
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
+  const int64_t G = a.Hq / a.Hkv;
+  const int64_t rows = a.B * a.Hq * a.T;
+  hipLaunchKernelGGL(moda_bwd_delta, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, s, a);
+  const int64_t tq = DQ_ROWS / G;
+  const int64_t dq_grid = (a.T + tq - 1) / tq * a.B * a.Hkv;
+  hipLaunchKernelGGL(moda_bwd_dq, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
+  const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv;
+  hipLaunchKernelGGL(moda_bwd_dkdv, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moda

@@ -29,6 +29,17 @@ constexpr int kModeCausal = 0;
 constexpr int kModeModa = 1;
 constexpr int kModeDepth = 2;
 
+struct BwdArgs {
+  const void *q, *k, *v, *packed, *kd, *vd, *out, *dout;
+  const float *lse;
+  float *delta;  // [B,Hq,T] scratch: <dO, O> per query row
+  void *dq, *dk, *dv, *dkd, *dvd;
+  int64_t B, Hq, Hkv, T, L, d;
+  int64_t nblk;      // packed depth blocks per (b, kv head)
+  float scale_log2;  // log2(e) / sqrt(d)
+  float scale;       // 1 / sqrt(d)
+};
+
 struct PackArgs {
   const void *kd, *vd;
   void *packed;
@@ -39,6 +50,9 @@ struct PackArgs {
 // MFMA path: dtype bf16, d == 128, G divides 32.
 hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s);
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
+
+// Backward, bf16, d == 128, G <= 64: delta, dQ, then dK/dV.
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
 // Generic path: fp32 or bf16, d in {32, 64, 128}, any G.
 hipError_t launch_fwd_generic(const FwdArgs &a, bool bf16, hipStream_t s);

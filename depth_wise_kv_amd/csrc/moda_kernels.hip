@@ -24,31 +24,11 @@
 
 #include <type_traits>
 
+#include "moda_device.h"
 #include "moda_internal.h"
 
 
 namespace moda {
-
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
-typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
-typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return float_to_bf16_bits(lo) | (float_to_bf16_bits(hi) << 16);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_swap32(float x) {
   // value held by lane (l ^ 32)
@@ -73,31 +53,6 @@ constexpr int D = kMfmaD;             // 128
 constexpr int M = kMfmaRows;          // 256 query rows per workgroup
 constexpr int NKEY = 64;              // keys per sequence tile
 constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
-
-typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
-typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
-
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// max / sum of x over the lane pair (l, l ^ 32) that shares one query row
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ shortx4 lds_read_tr(const char *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(const_cast<char *>(p)));
-}
 
 // Optional cycle tracing of the fused kernel's phases (off unless the build
 // defines MODA_TRACE_ENABLED; then moda_trace_buf receives per-phase cycle
@@ -226,7 +181,6 @@ static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divi
 // consecutive MFMAs independent.
 __device__ __forceinline__ constexpr int pv_order(int i) { return 4 * (i & 3) + (i >> 2); }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <int MODE>
 __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {

@@ -23,8 +23,8 @@ MODA_F32, MODA_BF16 = 0, 1
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
-           "moda_causal_fwd", "moda_depth_fwd", "moda_status_string", "moda_last_error",
-           "moda_fwd_variant")
+           "moda_causal_fwd", "moda_depth_fwd", "moda_bwd", "moda_status_string",
+           "moda_last_error", "moda_fwd_variant")
 
 
 class ModaShape(ctypes.Structure):
@@ -57,6 +57,9 @@ def _load():
     lib.moda_causal_fwd.restype = ctypes.c_int
     lib.moda_depth_fwd.argtypes = [sp, vp, vp, sz, vp, vp, vp]
     lib.moda_depth_fwd.restype = ctypes.c_int
+    lib.moda_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                             vp]
+    lib.moda_bwd.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     lib.moda_last_error.argtypes = []
@@ -118,6 +121,13 @@ def moda_causal_fwd(shape, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream):
 def moda_depth_fwd(shape, q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr, stream):
     return lib.moda_depth_fwd(_sref(shape), q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr,
                               stream)
+
+
+def moda_bwd(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes, out_ptr,
+             lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dkd_ptr, dvd_ptr, delta_ptr, stream):
+    return lib.moda_bwd(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes,
+                        out_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dkd_ptr, dvd_ptr,
+                        delta_ptr, stream)
 
 
 def moda_status_string(status: int) -> str:
@@ -226,6 +236,28 @@ def depth_forward(q, kd, vd, *, with_lse: bool = False):
     shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     packed = pack_depth_cache(kd, vd, shape)
     return depth_fwd(q, packed, Hkv, L, with_lse=with_lse)
+
+
+def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, delta=None):
+    """MoDA backward.  ``out`` and ``lse`` come from fwd(..., with_lse=True) on
+    the same inputs.  Returns (dq, dk, dv, dkd, dvd); dkd, dvd are None when
+    L = 0.  ``grads`` may pass the five output tensors to fill."""
+    import torch
+    _check_tensors(q, k, v, out, lse, dout, kd, vd, packed)
+    B, Hq, T, d = q.shape
+    L = 0 if kd is None else kd.shape[3]
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty_like(kd) if L else None, torch.empty_like(vd) if L else None)
+    if delta is None:
+        delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    nbytes = 0 if packed is None else packed.numel() * packed.element_size()
+    dq, dk, dv, dkd, dvd = grads
+    _check(moda_bwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(packed), nbytes,
+                    _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
+                    _ptr(dvd), _ptr(delta), _stream_ptr(q)), "moda_bwd")
+    return grads
 
 
 def moda_forward(q, k, v, kd=None, vd=None, *, with_lse: bool = False):

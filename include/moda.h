@@ -128,6 +128,32 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
                            size_t packed_bytes, void *out, float *lse,
                            void *hip_stream);
 
+/* MoDA backward: gradients of a loss with respect to Q, K, V and the depth
+ * keys and values, given dO (the loss gradient with respect to O) and the
+ * forward's O and LSE.  The chain rule through the forward's one softmax over
+ * sequence and depth entries (hyper.ai page on arXiv 2603.15619, section
+ * "Mixture-of-Depths Attention (MoDA)"); the depth entries' gradients follow
+ * the same rule with their own token's rows only.
+ *
+ *   q, k, v          : as for moda_fwd (read only)
+ *   k_depth, v_depth : depth K, V [B, Hkv, T, L, d] (read only; NULL if L == 0)
+ *   packed           : the packed depth cache of the same shape (NULL if L == 0)
+ *   out, lse         : O and LSE written by moda_fwd for these inputs (read only)
+ *   dout             : dO [B, Hq, T, d] (read only)
+ *   dq               : dQ [B, Hq, T, d], written in full
+ *   dk, dv           : dK, dV [B, Hkv, T, d], written in full (summed over the
+ *                      G query heads of each KV head)
+ *   dk_depth, dv_depth: dKd, dVd [B, Hkv, T, L, d], written in full (NULL if L == 0)
+ *   delta            : scratch [B, Hq, T] float32 that the call overwrites
+ * Gradients are bf16 (fp32 accumulation).  Supports bf16 with d = 128 and
+ * G = Hq / Hkv up to 64 (MODA_ERR_UNSUPPORTED otherwise).  Same validation,
+ * ownership and asynchrony rules as moda_fwd. */
+moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const void *v,
+                     const void *k_depth, const void *v_depth, const void *packed,
+                     size_t packed_bytes, const void *out, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, void *dk_depth,
+                     void *dv_depth, float *delta, void *hip_stream);
+
 /* Static text of a status code (never NULL). */
 const char *moda_status_string(moda_status st);
 

@@ -346,3 +346,44 @@ def test_runs_on_nondefault_stream(m, dev):
     s.synchronize()
     ref, _ = oracle.moda_forward(h_in["q"], h_in["k"], h_in["v"], h_in["kd"], h_in["vd"])
     assert max_err(out_to_f64(out), ref) <= BF16_TOL
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_SHAPES = [  # (B, Hq, Hkv, T, L): G = 1, 2, 3, 4, 8; ragged T
+    (1, 4, 4, 70, 0), (1, 8, 2, 130, 0), (2, 16, 4, 257, 0), (1, 8, 1, 100, 0), (1, 6, 2, 65, 0),
+    (1, 2, 2, 1, 0),
+]
+BWD_TOL = 2e-2  # max-abs error relative to max(1, max |reference|) of each gradient
+
+
+def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
+    from synth import f32_to_bf16_bits
+    from gpu_util import to_dev
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=seed)
+    h_in, d_in = host_case(cfg, dev)
+    rng = np.random.default_rng(seed + 1)
+    h_do = f32_to_bf16_bits(rng.standard_normal((B, Hq, T, 128)).astype(np.float32))
+    d_do = to_dev(h_do, "bf16", dev)
+    kd, vd = (d_in["kd"], d_in["vd"]) if L else (None, None)
+    packed = m.pack_depth_cache(kd, vd, m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) if L else None
+    out, lse = m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
+    grads = m.bwd(d_in["q"], d_in["k"], d_in["v"], out, lse, d_do, kd, vd, packed)
+    torch.cuda.synchronize()
+    ref = oracle.moda_backward(h_in["q"], h_in["k"], h_in["v"], h_in["kd"] if L else None,
+                               h_in["vd"] if L else None, h_do)
+    for name, g, r in zip(("dq", "dk", "dv", "dkd", "dvd"), grads, ref):
+        if r is None:
+            continue
+        scale = max(1.0, float(np.max(np.abs(r))))
+        e = max_err(out_to_f64(g), r)
+        print(f"[parity] bwd {B,Hq,Hkv,T,L} {name} max|err|={e:.3e} max|ref|={scale:.3e}",
+              flush=True)
+        assert e <= BWD_TOL * scale, f"{name}: {e} > {BWD_TOL} * {scale}"
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", BWD_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in BWD_SHAPES])
+def test_bwd_parity(m, dev, B, Hq, Hkv, T, L):
+    """moda_bwd against the oracle's backward, every element of every gradient."""
+    bwd_check(m, dev, B, Hq, Hkv, T, L, seed=300 + T + 7 * Hq)
