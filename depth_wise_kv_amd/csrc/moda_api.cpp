@@ -242,7 +242,20 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
   if (st != MODA_OK) return st;
   if (!use_mfma(s)) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports bf16 with d = 128");
   if (s->Hq / s->Hkv > 64) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports G up to 64");
-  if (s->L > 0) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd: depth gradients not built yet");
+  if (s->Hq / s->Hkv * s->T >= ((int64_t)1 << 23))
+    return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports G * T below 2^23");
+  if (s->L > 0) {
+    if (s->Hq / s->Hkv > 32)
+      return fail(MODA_ERR_UNSUPPORTED, "moda_bwd with depth entries supports G up to 32");
+    if (s->T * s->L >= ((int64_t)1 << 23))
+      return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports T * L below 2^23");
+    if (!k_depth || !v_depth || !dk_depth || !dv_depth)
+      return fail(MODA_ERR_INVALID_ARG, "depth inputs and gradients must be non-NULL when L > 0");
+    if (!aligned16(k_depth) || !aligned16(v_depth) || !aligned16(dk_depth) || !aligned16(dv_depth))
+      return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    st = check_packed(s, packed, packed_bytes);
+    if (st != MODA_OK) return st;
+  }
   st = check_qkvo(q, k, v, out, lse);
   if (st != MODA_OK) return st;
   if (!lse || !dout || !dq || !dk || !dv || !delta)

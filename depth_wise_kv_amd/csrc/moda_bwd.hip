@@ -141,6 +141,7 @@ __global__ __launch_bounds__(256) void moda_bwd_delta(BwdArgs p) {
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_ROWS = 32 * DQ_WAVES;  // 256
 
+template <bool HAS_DEPTH>
 __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = DQ_ROWS / G;
@@ -333,6 +334,103 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
     } else {
       if (mk) body(j, I0{}, std::true_type{});
       else body(j, I0{}, std::false_type{});
+    }
+  }
+
+  // ---------------- depth part of dQ: this wave's tokens' depth entries.
+  // Per 32-entry block: S_d^T = Kd Q^T (packed K half), P_d^T, dP_d^T = Vd dO^T
+  // (natural Vd rows), dS_d^T, then dQ^T += Kd^T dS_d^T with Kd^T read
+  // transposed from the block's natural Kd rows, loaded into this wave's
+  // 8 KiB of the (now idle) tile buffers.  Entries of other tokens in a block
+  // get weight 0.
+  if constexpr (HAS_DEPTH) {
+    const int64_t L = p.L;
+    const int64_t wt_lo = t0 + (wave * 32) / G;
+    int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;
+    if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
+    if (wt_hi > T) wt_hi = T;
+    if (L > 0 && wt_lo < wt_hi) {
+      const int64_t TL = T * L;
+      const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
+      const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
+      char *const slot = (wave < 2 ? kn0 : wave < 4 ? kn1 : wave < 6 ? kt0 : kt1) +
+                         (wave & 1) * (BTILE / 2);
+      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
+      const __bf16 *vnat = (const __bf16 *)p.vd + bh * TL * BD;
+      const __amdgpu_buffer_rsrc_t kd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const char *)p.kd + bh * TL * (BD * 2)), (short)0, (int)(TL * (BD * 2)),
+          0x00020000);
+      const int64_t my_lo = tok * L;
+      for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+        // natural Kd rows of the block into the slot, column-swizzled
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          dma16(kd_rsrc, slot + 4 * i * 256,
+                (uint32_t)(row * 256 + 16 * col_swz(row, lane & 15)),
+                (uint32_t)(blk * kDepthBlock * 256));
+        }
+        // S_d^T from the packed K half
+        floatx16 sd;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sd[rr] = init_s;
+        {
+          u32x4 kd[8];
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]),
+                                                         qb[ks], sd, 0, 0, 0);
+        }
+        // register rr holds entry blk*32 + 8*(rr/4) + 4*lh + rr%4: keep it iff
+        // it is one of this row's token's entries
+        {
+          const int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
+          const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[rr] = -INFINITY;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sd[rr] = fast_exp2(c * sd[rr]);
+        // dP_d^T = Vd dO^T - D from the natural Vd rows (entry lane%32)
+        floatx16 dpd;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) dpd[rr] = init_dp;
+        {
+          const int64_t e = blk * kDepthBlock + li;
+          const bool e_ok = e < TL;
+          u32x4 vr[8];
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            vr[ks] = e_ok ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[ks]),
+                                                          gb[ks], dpd, 0, 0, 0);
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = 8 * kk + 2 * q;
+            w[q] = cvt_bf16x2(sd[rr] * dpd[rr], sd[rr + 1] * dpd[rr + 1]);
+          }
+          dsb[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+        wait_vmem();  // the Kd rows have landed in the slot
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb + kk),
+                                                             dsb[kk], dq[nb], 0, 0, 0);
+      }
     }
   }
 
@@ -567,15 +665,181 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dKd, dVd: depth entries' gradients.  8 waves; a wave owns TW = floor(32/G)
+// whole tokens (their G query rows each), so every row that reads an entry
+// is in the entry's wave.  Per 32-entry block of the wave's span, with a lane
+// owning an entry: S_d = Q Kd^T (packed K half), P_d, dP_d = dO Vd^T (natural
+// Vd rows), dS_d; dVd^T = dO^T P_d and dKd^T = Q^T dS_d with Q^T and dO^T read
+// transposed from this wave's own rows, stored once in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
+  const int G = (int)(p.Hq / p.Hkv);
+  const int TW = 32 / G;            // tokens per wave (G <= 32)
+  const int TWG = TW * DQ_WAVES;    // tokens per workgroup
+  __shared__ __attribute__((aligned(1024))) char q_s[DQ_WAVES][32 * 256];
+  __shared__ __attribute__((aligned(1024))) char g_s[DQ_WAVES][32 * 256];
+  __shared__ __attribute__((aligned(16))) float lse_s[DQ_WAVES][32];
+  __shared__ __attribute__((aligned(16))) float del_s[DQ_WAVES][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5;
+  const TileFrags fr(lane);
+
+  const int64_t T = p.T, L = p.L, TL = p.T * p.L;
+  const int64_t BH = p.B * p.Hkv;
+  const int64_t x = blockIdx.x;
+  const int64_t bh = x % BH;
+  const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const int64_t wt_lo = (x / BH) * TWG + (int64_t)wave * TW;  // this wave's first token
+  int64_t wt_hi = wt_lo + TW;
+  if (wt_hi > T) wt_hi = T;
+
+  // this lane's row (as an A operand and for the LDS copies): row li
+  const int r = li;
+  const bool row_used = r < TW * G;
+  const int64_t tok = wt_lo + r / G;
+  const bool row_ok = row_used && tok < T;
+  const int64_t head = hkv * G + (row_used ? r % G : 0);
+  const int64_t qrow = (b * p.Hq + head) * T + (row_ok ? tok : 0);
+  bf16x8 qb[8], gb[8];
+  load_row_operand((const __bf16 *)p.q + qrow * BD, row_ok, lh, qb);
+  load_row_operand((const __bf16 *)p.dout + qrow * BD, row_ok, lh, gb);
+  // the wave's rows into LDS, column-swizzled, for the transposed products
+  char *const qs = q_s[wave];
+  char *const gs = g_s[wave];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int chunk = 8 * lh + ks;
+    const int off = r * 256 + 16 * (chunk ^ (4 * (r & 3)));
+    *(bf16x8 *)(qs + off) = qb[ks];
+    *(bf16x8 *)(gs + off) = gb[ks];
+  }
+  if (lh == 0) {
+    lse_s[wave][r] = row_ok ? p.lse[qrow] * LOG2E : INFINITY;
+    del_s[wave][r] = row_ok ? p.delta[qrow] : 0.f;
+  }
+  __syncthreads();
+  if (wt_lo >= T) return;
+
+  const float c = p.scale_log2;
+  const float neg_inv_c = -1.0f / c;
+  const int64_t e_lo = wt_lo * L, e_hi = wt_hi * L;  // entries this wave owns
+  const int64_t blk_lo = e_lo / kDepthBlock;
+  const int64_t blk_hi = (e_hi + kDepthBlock - 1) / kDepthBlock;
+  const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
+  const __bf16 *vnat = (const __bf16 *)p.vd + bh * TL * BD;
+  // per register rr of a block: row 8*(rr/4) + 4*lh + rr%4, its token offset
+  // and its lse2 / D
+  float init_s[16], init_dp[16];
+  int rtok[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int row0 = 8 * g + 4 * lh;
+    const float4 l4 = *(const float4 *)&lse_s[wave][row0];
+    const float4 d4 = *(const float4 *)&del_s[wave][row0];
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      init_s[4 * g + i] = lv[i] * neg_inv_c;
+      init_dp[4 * g + i] = -dv4[i];
+      const int row = row0 + i;
+      rtok[4 * g + i] = row < TW * G ? row / G : -1;  // -1: an idle row
+    }
+  }
+
+  for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+    const int64_t e = blk * kDepthBlock + li;  // this lane's entry
+    // S_d = Q Kd^T (rows x entries)
+    floatx16 sd;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sd[rr] = init_s[rr];
+    {
+      u32x4 kd[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]),
+                                                     sd, 0, 0, 0);
+    }
+    // keep (row, entry) iff the entry is one of the row's token's entries
+    const int64_t etok = e / L - wt_lo;  // the entry's token, relative
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      if (rtok[rr] < 0 || (int64_t)rtok[rr] != etok || e >= e_hi) sd[rr] = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sd[rr] = fast_exp2(c * sd[rr]);
+    // dP_d = dO Vd^T - D
+    floatx16 dpd;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) dpd[rr] = init_dp[rr];
+    {
+      const bool e_ok = e < TL;
+      u32x4 vr[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        vr[ks] = e_ok ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
+                                                      dpd, 0, 0, 0);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 w, wd;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = 8 * kk + 2 * q;
+        w[q] = cvt_bf16x2(sd[rr], sd[rr + 1]);
+        wd[q] = cvt_bf16x2(sd[rr] * dpd[rr], sd[rr + 1] * dpd[rr + 1]);
+      }
+      pb[kk] = __builtin_bit_cast(bf16x8, w);
+      dsb[kk] = __builtin_bit_cast(bf16x8, wd);
+    }
+    // dVd^T = dO^T P_d ; dKd^T = Q^T dS_d  (the wave's 32 rows as two k-steps)
+    floatx16 dvd[4], dkd[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) dvd[nb][rr] = dkd[nb][rr] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        dvd[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(gs, 4 * nb + kk), pb[kk],
+                                                          dvd[nb], 0, 0, 0);
+        dkd[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(qs, 4 * nb + kk), dsb[kk],
+                                                          dkd[nb], 0, 0, 0);
+      }
+    if (e >= e_lo && e < e_hi) {
+      store_row((__bf16 *)p.dkd + (bh * TL + e) * BD, dkd, p.scale, lh);
+      store_row((__bf16 *)p.dvd + (bh * TL + e) * BD, dvd, 1.0f, lh);
+    }
+  }
+}
+
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int64_t G = a.Hq / a.Hkv;
   const int64_t rows = a.B * a.Hq * a.T;
   hipLaunchKernelGGL(moda_bwd_delta, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, s, a);
   const int64_t tq = DQ_ROWS / G;
   const int64_t dq_grid = (a.T + tq - 1) / tq * a.B * a.Hkv;
-  hipLaunchKernelGGL(moda_bwd_dq, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
+  if (a.L > 0)
+    hipLaunchKernelGGL(moda_bwd_dq<true>, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL(moda_bwd_dq<false>, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
   const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv;
   hipLaunchKernelGGL(moda_bwd_dkdv, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
+  if (a.L > 0) {
+    const int64_t twg = (32 / G) * DQ_WAVES;
+    const int64_t dd_grid = (a.T + twg - 1) / twg * a.B * a.Hkv;
+    hipLaunchKernelGGL(moda_bwd_ddepth, dim3((uint32_t)dd_grid), dim3(64 * DQ_WAVES), 0, s, a);
+  }
   return hipGetLastError();
 }
 
