@@ -11,7 +11,9 @@ the same packed cache for its HBM rate.  Prints one JSON line.
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
 
 FLOP convention (algorithmic, per query head): 4 * d * (T(T+1)/2 + T*L), the
-diagonal counted, exponentials not counted.
+diagonal counted, exponentials not counted.  The backward (moda_bwd, timed
+after the step, not part of it) is credited 2.5x that: five products per
+(query, entry) pair (S recomputed, dP, dV, dQ, dK) against the forward's two.
 """
 from __future__ import annotations
 
@@ -150,7 +152,7 @@ def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
                       f"full workload extrapolated to {full_s:.0f} s"}
 
 
-def bench_config(cfg, steps, warmup, with_cpu, causal=True):
+def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
     import torch
     from depth_wise_kv_amd import moda
     from synth import torch_inputs
@@ -200,8 +202,26 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True):
         moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout)
         depth_ms = float(np.mean(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
                                        steps, stream)))
+    bwd_ms = None
+    if with_bwd and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["Hq"] // cfg["Hkv"] <= 32:
+        # backward of the same step: O, LSE from the forward, a seeded dO
+        o_b, lse_b = moda.fwd(q, k, v, packed, L, with_lse=True)
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.get("seed", 0) + 5)
+        dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty_like(kd) if L else None, torch.empty_like(vd) if L else None)
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+        def bwd():
+            moda.bwd(q, k, v, o_b, lse_b, dout, kd if L else None, vd if L else None, packed,
+                     grads=grads, delta=delta)
+
+        bwd()
+        bwd_ms = float(np.mean(timed(bwd, steps, stream)))
+        del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
-               depth_ms=depth_ms)
+               depth_ms=depth_ms, bwd_ms=bwd_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -220,6 +240,10 @@ def profile_only(cfg, which, steps):
     shape = moda.make_shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], L, cfg["d"], cfg["dtype"])
     packed = moda.pack_depth_cache(d_in["kd"], d_in["vd"], shape) if L else None
     out = torch.empty_like(d_in["q"])
+    if which == "bwd":
+        o_b, lse_b = moda.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
+        dout = torch.randn_like(d_in["q"], dtype=torch.float32).to(d_in["q"].dtype)
+        kd, vd = (d_in["kd"], d_in["vd"]) if L else (None, None)
     torch.cuda.synchronize()
     for _ in range(steps):
         if which == "fwd":
@@ -228,6 +252,8 @@ def profile_only(cfg, which, steps):
             moda.causal_fwd(d_in["q"], d_in["k"], d_in["v"], out=out)
         elif which == "depth":
             moda.depth_fwd(d_in["q"], packed, cfg["Hkv"], L, out=out)
+        elif which == "bwd":
+            moda.bwd(d_in["q"], d_in["k"], d_in["v"], o_b, lse_b, dout, kd, vd, packed)
         else:
             moda.pack_depth_cache(d_in["kd"], d_in["vd"], shape, out=packed)
     torch.cuda.synchronize()
@@ -244,7 +270,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--only", default=None,
                     help="with --sweep: run only points whose name contains this string")
-    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth"],
+    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
                     help="time a bf16 N x N x N torch.matmul (hipBLASLt): the practical "
@@ -311,7 +337,7 @@ def main():
         for c in sweep_points():
             if args.only and args.only not in c["name"]:
                 continue
-            r = bench_config(c, args.steps, args.warmup, False, causal=True)
+            r = bench_config(c, args.steps, args.warmup, False, causal=True, with_bwd=False)
             print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
                               "pack_ms": r["pack_ms"], "causal_ms": r["causal_ms"],
@@ -359,6 +385,8 @@ def main():
         "fwd_hbm_gbs": fused_bytes(cfg) / r["fwd_ms"] / 1e6,
         "depth_only_ms": r["depth_ms"],
         "depth_only_hbm_gbs": depth_bytes(cfg) / r["depth_ms"] / 1e6 if r["depth_ms"] else None,
+        "bwd_ms": r["bwd_ms"],
+        "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
         "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:

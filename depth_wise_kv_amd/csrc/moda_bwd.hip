@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   wait_vmem();
   __syncthreads();
 
-  auto body = [&](int j, auto parity, auto masked) {
+  auto body = [&](int j, auto parity, bool masked) {
     constexpr int P = decltype(parity)::value;
     const char *const kn_rd = P ? kn1 : kn0;
     const char *const kt_rd = P ? kt1 : kt0;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (decltype(masked)::value) mask_half(s, j, kb2);
+      if (masked) mask_half(s, j, kb2);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
       // dP^T = V dO^T (from -D)
@@ -323,18 +323,12 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   const int n_nm = (int)min((int64_t)n_kt, (wave_tok_lo + 1) / 64);
   int j = 0;
   for (; j + 1 < n_nm; j += 2) {
-    body(j, I0{}, std::false_type{});
-    body(j + 1, I1{}, std::false_type{});
+    body(j, I0{}, false);
+    body(j + 1, I1{}, false);
   }
   for (; j < n_kt; ++j) {
-    const bool mk = j >= n_nm;
-    if (j & 1) {
-      if (mk) body(j, I1{}, std::true_type{});
-      else body(j, I1{}, std::false_type{});
-    } else {
-      if (mk) body(j, I0{}, std::true_type{});
-      else body(j, I0{}, std::false_type{});
-    }
+    if (j & 1) body(j, I1{}, j >= n_nm);
+    else body(j, I0{}, j >= n_nm);
   }
 
   // ---------------- depth part of dQ: this wave's tokens' depth entries.
@@ -731,31 +725,25 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   const int64_t blk_hi = (e_hi + kDepthBlock - 1) / kDepthBlock;
   const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
   const __bf16 *vnat = (const __bf16 *)p.vd + bh * TL * BD;
-  // per register rr of a block: row 8*(rr/4) + 4*lh + rr%4, its token offset
-  // and its lse2 / D
-  float init_s[16], init_dp[16];
-  int rtok[16];
+  // register rr of a block holds row 8*(rr/4) + 4*lh + rr%4; its lse2 and D
+  // are read from LDS when needed
+  auto row_init = [&](const float (*buf)[32], float mul, floatx16 &acc) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int row0 = 8 * g + 4 * lh;
-    const float4 l4 = *(const float4 *)&lse_s[wave][row0];
-    const float4 d4 = *(const float4 *)&del_s[wave][row0];
-    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      init_s[4 * g + i] = lv[i] * neg_inv_c;
-      init_dp[4 * g + i] = -dv4[i];
-      const int row = row0 + i;
-      rtok[4 * g + i] = row < TW * G ? row / G : -1;  // -1: an idle row
+    for (int g = 0; g < 4; ++g) {
+      const float4 v4 = *(const float4 *)&buf[wave][8 * g + 4 * lh];
+      acc[4 * g + 0] = v4.x * mul;
+      acc[4 * g + 1] = v4.y * mul;
+      acc[4 * g + 2] = v4.z * mul;
+      acc[4 * g + 3] = v4.w * mul;
     }
-  }
+  };
+  const int tw_rows = TW * G;
 
   for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
     const int64_t e = blk * kDepthBlock + li;  // this lane's entry
     // S_d = Q Kd^T (rows x entries)
     floatx16 sd;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sd[rr] = init_s[rr];
+    row_init(lse_s, neg_inv_c, sd);
     {
       u32x4 kd[8];
 #pragma unroll
@@ -769,14 +757,15 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
     // keep (row, entry) iff the entry is one of the row's token's entries
     const int64_t etok = e / L - wt_lo;  // the entry's token, relative
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-      if (rtok[rr] < 0 || (int64_t)rtok[rr] != etok || e >= e_hi) sd[rr] = -INFINITY;
+    for (int rr = 0; rr < 16; ++rr) {
+      const int row = 8 * (rr >> 2) + 4 * lh + (rr & 3);
+      if (row >= tw_rows || (int64_t)(row / G) != etok || e >= e_hi) sd[rr] = -INFINITY;
+    }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sd[rr] = fast_exp2(c * sd[rr]);
     // dP_d = dO Vd^T - D
     floatx16 dpd;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) dpd[rr] = init_dp[rr];
+    row_init(del_s, -1.0f, dpd);
     {
       const bool e_ok = e < TL;
       u32x4 vr[8];
@@ -801,24 +790,26 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
       pb[kk] = __builtin_bit_cast(bf16x8, w);
       dsb[kk] = __builtin_bit_cast(bf16x8, wd);
     }
-    // dVd^T = dO^T P_d ; dKd^T = Q^T dS_d  (the wave's 32 rows as two k-steps)
-    floatx16 dvd[4], dkd[4];
+    // dVd^T = dO^T P_d, then dKd^T = Q^T dS_d (the wave's 32 rows as two
+    // k-steps), one accumulator set at a time
+    const bool owned = e >= e_lo && e < e_hi;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int which = 0; which < 2; ++which) {
+      floatx16 acc[4];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) dvd[nb][rr] = dkd[nb][rr] = 0.f;
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+        for (int rr = 0; rr < 16; ++rr) acc[nb][rr] = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        dvd[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(gs, 4 * nb + kk), pb[kk],
-                                                          dvd[nb], 0, 0, 0);
-        dkd[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(qs, 4 * nb + kk), dsb[kk],
-                                                          dkd[nb], 0, 0, 0);
-      }
-    if (e >= e_lo && e < e_hi) {
-      store_row((__bf16 *)p.dkd + (bh * TL + e) * BD, dkd, p.scale, lh);
-      store_row((__bf16 *)p.dvd + (bh * TL + e) * BD, dvd, 1.0f, lh);
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              fr.colfrag(which ? qs : gs, 4 * nb + kk), which ? dsb[kk] : pb[kk], acc[nb], 0, 0,
+              0);
+      if (owned)
+        store_row((__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + e) * BD, acc,
+                  which ? p.scale : 1.0f, lh);
     }
   }
 }
