@@ -251,42 +251,36 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
     // j+1 are spread between the first half's MFMAs.
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      // S^T = K Q^T (from -lse2/c) for keys 32*kb2 .. +31
-      floatx16 s;
+      // S^T = K Q^T (from -lse2/c) and dP^T = V dO^T (from -D) for keys
+      // 32*kb2 .. +31: two independent MFMA chains, interleaved
+      floatx16 s, dp;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[rr] = init_s;
+      for (int rr = 0; rr < 16; ++rr) {
+        s[rr] = init_s;
+        dp[rr] = init_dp;
+      }
       {
-        bf16x8 a[4];
+        bf16x8 a[4], av[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = fr.rowfrag(kn_rd, 2 * i + kb2);
+        for (int i = 0; i < 2; ++i) {
+          a[i] = fr.rowfrag(kn_rd, 2 * i + kb2);
+          av[i] = fr.rowfrag(vn_rd, 2 * i + kb2);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 3], qb[ks], s, 0, 0, 0);
-          if (ks + 4 < 8) a[ks & 3] = fr.rowfrag(kn_rd, 2 * (ks + 4) + kb2);
+          if (ks + 2 < 8) a[(ks + 2) & 3] = fr.rowfrag(kn_rd, 2 * (ks + 2) + kb2);
           if (kb2 == 0 && ks < 6) dma_one(ks, j + 1, kn_wr, kt_wr, vn_wr);
+          __builtin_amdgcn_sched_barrier(0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 3], gb[ks], dp, 0, 0, 0);
+          if (ks + 2 < 8) av[(ks + 2) & 3] = fr.rowfrag(vn_rd, 2 * (ks + 2) + kb2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (masked) mask_half(s, j, kb2);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
-      // dP^T = V dO^T (from -D)
-      floatx16 dp;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) dp[rr] = init_dp;
-      {
-        bf16x8 a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = fr.rowfrag(vn_rd, 2 * i + kb2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 3], gb[ks], dp, 0, 0, 0);
-          if (ks + 4 < 8) a[ks & 3] = fr.rowfrag(vn_rd, 2 * (ks + 4) + kb2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
       // dS^T = P^T (dP^T - D) as bf16 B operands of k-steps 2*kb2, 2*kb2 + 1
       bf16x8 dsb[2];
 #pragma unroll
@@ -434,9 +428,14 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
 // ---------------------------------------------------------------------------
 // dK, dV: 4 waves x 32 sequence keys, query tiles of 64 rows.
 // ---------------------------------------------------------------------------
-constexpr int KV_WAVES = 4;
-constexpr int KV_KEYS = 32 * KV_WAVES;  // 128
+#ifndef MODA_BWD_KV_WAVES
+#define MODA_BWD_KV_WAVES 4
+#endif
+constexpr int KV_WAVES = MODA_BWD_KV_WAVES;
+constexpr int KV_KEYS = 32 * KV_WAVES;
 constexpr int QROWS = 64;
+constexpr int KV_ROWS = QROWS / KV_WAVES;  // query tile rows each wave loads
+constexpr int KV_DMA = KV_ROWS / 4;        // 4-row load instructions per copy
 
 __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
@@ -485,8 +484,8 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int64_t n_qt = (T - k0 + TQr - 1) / TQr;
 
   // Tile loads.  Tile row r holds token t0 + r / G of head hkv*G + r % G; this
-  // wave loads rows 16*wave .. +15 of Q and of dO, each twice (row- and
-  // column-swizzled): 4 instructions of 4 rows per copy.  Rows past the
+  // wave loads rows KV_ROWS*wave .. +KV_ROWS-1 of Q and of dO, each twice
+  // (row- and column-swizzled), in instructions of 4 rows.  Rows past the
   // tile's tokens point outside the descriptor range and read as zeros.
   const int64_t grp = b * p.Hq + hkv * G;  // first query head row block of the group
   const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -495,10 +494,10 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.dout + grp * T * (BD * 2)), (short)0, (int)(G * T * (BD * 2)),
       0x00020000);
-  uint32_t off_r[4], off_c[4];
+  uint32_t off_r[KV_DMA], off_c[KV_DMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < KV_DMA; ++i) {
+    const int row = KV_ROWS * wave + 4 * i + (lane >> 4);
     const bool used = row < TQr * G;
     const uint32_t base = (uint32_t)(((row % G) * T + row / G) * 256);
     off_r[i] = used ? base + 16 * row_swz(row, lane & 15) : 0x80000000u;
@@ -507,8 +506,8 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   auto dma_tile = [&](int64_t qt, char *qn, char *qtr, char *gn, char *gtr) {
     const uint32_t soff = (uint32_t)((k0 + qt * TQr) * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lrow = (16 * wave + 4 * i) * 256;
+    for (int i = 0; i < KV_DMA; ++i) {
+      const int lrow = (KV_ROWS * wave + 4 * i) * 256;
       dma16(q_rsrc, qn + lrow, off_r[i], soff);
       dma16(q_rsrc, qtr + lrow, off_c[i], soff);
       dma16(g_rsrc, gn + lrow, off_r[i], soff);
@@ -586,11 +585,15 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         dpv[4 * g + 2] = -d4.z;
         dpv[4 * g + 3] = -d4.w;
       }
-      // S = Q K^T (rows x keys)
+      // S = Q K^T and dP = dO V^T - D (rows x keys): two independent MFMA
+      // chains, interleaved
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(qn, 2 * ks + sb), kb[ks], s, 0, 0,
                                                     0);
+        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(gn, 2 * ks + sb), vb[ks], dpv, 0,
+                                                      0, 0);
+      }
       if (masked) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -610,11 +613,6 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         for (int q = 0; q < 4; ++q) w[q] = cvt_bf16x2(s[8 * kk + 2 * q], s[8 * kk + 2 * q + 1]);
         pb[kk] = __builtin_bit_cast(bf16x8, w);
       }
-      // dP = dO V^T - D
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(gn, 2 * ks + sb), vb[ks], dpv, 0,
-                                                      0, 0);
       bf16x8 dsb[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
