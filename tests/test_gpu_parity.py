@@ -389,3 +389,26 @@ def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
 def test_bwd_parity(m, dev, B, Hq, Hkv, T, L):
     """moda_bwd against the oracle's backward, every element of every gradient."""
     bwd_check(m, dev, B, Hq, Hkv, T, L, seed=300 + T + 7 * Hq)
+
+
+def test_bwd_layer_1p5b_full(m, dev):
+    """B2 Hq16 Hkv4 T4096 d128 L24 (bf16 N(0,1)*0.5 inputs, N(0,1) dO): every
+    element of every gradient against the oracle's backward."""
+    from synth import f32_to_bf16_bits
+    from gpu_util import to_dev
+    cfg = WORKLOADS["layer_1p5b"]
+    d_in = device_case(cfg, dev)
+    B, Hq, Hkv, T, L = (cfg[x] for x in ("B", "Hq", "Hkv", "T", "L"))
+    h_do = f32_to_bf16_bits(np.random.default_rng(2024).standard_normal((B, Hq, T, 128))
+                            .astype(np.float32))
+    d_do = to_dev(h_do, "bf16", dev)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"], m.make_shape(B, Hq, Hkv, T, L, 128, "bf16"))
+    out, lse = m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
+    grads = m.bwd(d_in["q"], d_in["k"], d_in["v"], out, lse, d_do, d_in["kd"], d_in["vd"], packed)
+    torch.cuda.synchronize()
+    ref = oracle.moda_backward(*(to_np(d_in[n]) for n in ("q", "k", "v", "kd", "vd")), h_do)
+    for name, g, r in zip(("dq", "dk", "dv", "dkd", "dvd"), grads, ref):
+        scale = max(1.0, float(np.max(np.abs(r))))
+        e = max_err(out_to_f64(g), r)
+        print(f"[parity] bwd layer_1p5b {name} max|err|={e:.3e} max|ref|={scale:.3e}", flush=True)
+        assert e <= BWD_TOL * scale
