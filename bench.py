@@ -33,7 +33,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoDA fwd TFLOP/s + % bf16 MFMA peak at T=64K; time ratio vs causal-only"
 KERNEL_SOURCES = [os.path.join(ROOT, "depth_wise_kv_amd", "csrc", f)
-                  for f in ("moda_kernels.hip", "moda_internal.h")]
+                  for f in ("moda_kernels.hip", "moda_device.h", "moda_internal.h")]
 
 
 def flops(c, L=None):
