@@ -4,8 +4,9 @@
 One step = the whole MoDA path over one batch of synthetic input already in
 HBM: moda_pack_depth_cache (depth repack) + moda_fwd (fused forward).  The
 causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
-MoDA / causal-only time ratio, and depth attention alone (moda_depth_fwd) on
-the same packed cache for its HBM rate.  Prints one JSON line.
+MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
+same packed cache for its HBM rate, and the forward straight from the natural
+depth layout (moda_fwd_natural) for the repack ablation.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
@@ -196,6 +197,12 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         cout = torch.empty_like(q)
         moda.causal_fwd(q, k, v, out=cout)
         causal_ms = float(np.mean(timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream)))
+    natural_ms = None
+    if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
+        nout = torch.empty_like(q)
+        moda.fwd_natural(q, k, v, kd, vd, out=nout)
+        natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
+                                         steps, stream)))
     depth_ms = None
     if L:
         dout = torch.empty_like(q)
@@ -221,7 +228,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
         del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
-               depth_ms=depth_ms, bwd_ms=bwd_ms)
+               depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -345,6 +352,7 @@ def main():
                               "causal_tflops": flops(c, 0) / r["causal_ms"] / 1e9,
                               "ratio_fwd_over_causal": r["fwd_ms"] / r["causal_ms"],
                               "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6,
+                              "fwd_natural_layout_ms": r["natural_ms"],
                               "depth_only_ms": r["depth_ms"],
                               "depth_only_hbm_gbs": (depth_bytes(c) / r["depth_ms"] / 1e6
                                                      if r["depth_ms"] else None)}), flush=True)
@@ -385,6 +393,7 @@ def main():
         "fwd_hbm_gbs": fused_bytes(cfg) / r["fwd_ms"] / 1e6,
         "depth_only_ms": r["depth_ms"],
         "depth_only_hbm_gbs": depth_bytes(cfg) / r["depth_ms"] / 1e6 if r["depth_ms"] else None,
+        "fwd_natural_layout_ms": r["natural_ms"],
         "bwd_ms": r["bwd_ms"],
         "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
         "roofline": roofline(cfg, r["fwd_ms"], traffic),

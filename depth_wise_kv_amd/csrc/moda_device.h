@@ -56,4 +56,41 @@ __device__ __forceinline__ shortx4 lds_read_tr(const char *p) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Per-lane LDS addressing for a 64-row tile of 256-byte rows.
+//   rowfrag(buf, i): A or B operand holding row 32*(i & 1) + lane%32, dims
+//                    64*(lane/32) + 8*(i >> 1) .. +7 (row-swizzled tile)
+//   colfrag(buf, i): A operand of a transposed product, i = 4*nb + kk: dims
+//                    32*nb + lane%32, the 8 rows of k-step kk that pair with
+//                    the register order of an MFMA result (column-swizzled)
+struct TileFrags {
+  int k_row, k_x;
+  int vaddr[4];
+  __device__ explicit TileFrags(int lane) {
+    const int li = lane & 31, lh = lane >> 5;
+    k_row = li * 256 + 16 * ((8 * lh) ^ (li & 8));
+    k_x = li & 7;
+    const int lg = lane >> 4, lq = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      vaddr[nb] = (4 * (lg >> 1) + (lq >> 2)) * 256 +
+                  16 * (4 * (nb ^ (lq >> 2)) + 2 * (lg & 1) + ((lq & 3) >> 1)) + 8 * (lq & 1);
+  }
+  __device__ bf16x8 rowfrag(const char *b, int i) const {
+    return *(const bf16x8 *)(b + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
+  }
+  __device__ bf16x8 colfrag(const char *b, int i) const {
+    const char *vp = b + vaddr[i >> 2] + 16 * (i & 3) * 256;
+    const shortx4 lo = lds_read_tr(vp);
+    const shortx4 hi = lds_read_tr(vp + 8 * 256);
+    return __builtin_bit_cast(
+        bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                        __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+  }
+};
+
+// 16-byte chunk that LDS slot `slot` of tile row `row` holds
+__device__ __forceinline__ int row_swz(int row, int slot) { return slot ^ (row & 15); }
+__device__ __forceinline__ int col_swz(int row, int slot) { return slot ^ (4 * (row & 3)); }
+
+
 }  // namespace moda

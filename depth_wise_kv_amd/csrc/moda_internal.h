@@ -15,6 +15,7 @@ constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part +
 
 struct FwdArgs {
   const void *q, *k, *v, *packed;
+  const void *kd_nat, *vd_nat;  // depth K, V in their natural layout (natural-layout mode)
   void *out;
   float *lse;
   int64_t B, Hq, Hkv, T, L, d;
@@ -28,6 +29,7 @@ struct FwdArgs {
 constexpr int kModeCausal = 0;
 constexpr int kModeModa = 1;
 constexpr int kModeDepth = 2;
+constexpr int kModeModaNatural = 3;  // MoDA reading depth K, V in their natural layout
 
 struct BwdArgs {
   const void *q, *k, *v, *packed, *kd, *vd, *out, *dout;

@@ -186,6 +186,7 @@ template <int MODE>
 __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   constexpr bool HAS_DEPTH = MODE != kModeCausal;  // depth entries are read
   constexpr bool HAS_SEQ = MODE != kModeDepth;     // sequence keys are read
+  constexpr bool NATURAL = MODE == kModeModaNatural;  // depth K, V in natural layout
   // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
@@ -241,6 +242,68 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   // Odd workgroups stream their depth span before the key loop, even ones
   // after it, so that at any time part of the chip streams depth blocks from
   // HBM while the rest runs the matrix-core-bound key loop.
+  // Depth blocks [blk_lo, blk_hi) read in the natural [B,Hkv,T,L,d] layout
+  // (the natural-layout mode): a block's 32 Kd rows load straight into MFMA
+  // operand registers (16 bytes of one row per lane), and its 32 Vd rows go
+  // into this wave's 8 KiB of the tile buffers, column-swizzled, to be read
+  // transposed as the A operand of O^T += Vd^T P^T.
+  auto depth_natural = [&](int64_t blk_lo, int64_t blk_hi, int64_t my_lo) {
+    if constexpr (NATURAL) {
+      const int64_t L = p.L, TL = T * L;
+      const __bf16 *knat = (const __bf16 *)p.kd_nat + bh * TL * D;
+      const __amdgpu_buffer_rsrc_t vd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const char *)p.vd_nat + bh * TL * (D * 2)), (short)0, (int)(TL * (D * 2)),
+          0x00020000);
+      char *const slot = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) +
+                         (wave & 1) * (TILE_BYTES / 2);
+      const TileFrags fr(lane);
+      auto load_k = [&](int64_t blk, u32x4 (&kd)[8]) {
+        const int64_t e = blk * kDepthBlock + li;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          kd[ks] = e < TL ? *(const u32x4 *)(knat + e * D + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+      };
+      u32x4 kd[8];
+      load_k(blk_lo, kd);
+      for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vd_rsrc, (__attribute__((address_space(3))) void *)(slot + 4 * i * 256), 16,
+              (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3)))),
+              (uint32_t)(blk * kDepthBlock * 256), 0, 0);
+        }
+        floatx16 sd[1];
+        floatx16 sd2[2] = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          sd2[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, kd[ks]), qb[ks], sd2[ks & 1], 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
+        const bool more = blk + 1 < blk_hi;
+        if (more) load_k(blk + 1, kd);
+        const int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
+        const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[0][rr] = -INFINITY;
+        bf16x8 pb[2];
+        softmax_update<1>(st, sd, p.scale_log2, pb);
+        // the Vd rows have landed (the next block's Kd loads may still be in flight)
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+        else wait_vmem();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb + kk),
+                                                                 pb[kk], st.acc[nb], 0, 0, 0);
+      }
+    }
+  };
   auto depth_part = [&]() {
     if constexpr (HAS_DEPTH) {
       const int64_t L = p.L;
@@ -251,8 +314,12 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
       if (L > 0 && wt_lo < wt_hi) {
         const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
         const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
-        const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
         const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
+        if constexpr (NATURAL) {
+          depth_natural(blk_lo, blk_hi, my_lo);
+          return;
+        }
+        const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
         u32x4 kd[8], vd[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
@@ -297,7 +364,11 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   };
   const bool depth_first = HAS_DEPTH && (!HAS_SEQ || (blockIdx.x & 1));
   MODA_TRACE_DECL
-  if (depth_first) depth_part();
+  if (depth_first) {
+    depth_part();
+    // the natural-layout depth loop used the tile buffers as per-wave slots
+    if constexpr (NATURAL && HAS_SEQ) __syncthreads();
+  }
 
   if constexpr (HAS_SEQ) {
     // ---------------- sequence part
@@ -650,7 +721,10 @@ hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t TQ = M / G;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const int64_t grid = ntiles * a.B * a.Hkv;
-  if (!a.has_seq)
+  if (a.kd_nat)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural>), dim3((uint32_t)grid), dim3(64 * NWAVE),
+                       0, s, a);
+  else if (!a.has_seq)
     hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
                        a);
   else if (a.has_depth)

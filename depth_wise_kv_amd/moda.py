@@ -23,8 +23,8 @@ MODA_F32, MODA_BF16 = 0, 1
 
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
-           "moda_causal_fwd", "moda_depth_fwd", "moda_bwd", "moda_status_string",
-           "moda_last_error", "moda_fwd_variant")
+           "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
+           "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
 class ModaShape(ctypes.Structure):
@@ -57,6 +57,8 @@ def _load():
     lib.moda_causal_fwd.restype = ctypes.c_int
     lib.moda_depth_fwd.argtypes = [sp, vp, vp, sz, vp, vp, vp]
     lib.moda_depth_fwd.restype = ctypes.c_int
+    lib.moda_fwd_natural.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moda_fwd_natural.restype = ctypes.c_int
     lib.moda_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                              vp]
     lib.moda_bwd.restype = ctypes.c_int
@@ -121,6 +123,11 @@ def moda_causal_fwd(shape, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, stream):
 def moda_depth_fwd(shape, q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr, stream):
     return lib.moda_depth_fwd(_sref(shape), q_ptr, packed_ptr, packed_bytes, out_ptr, lse_ptr,
                               stream)
+
+
+def moda_fwd_natural(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, stream):
+    return lib.moda_fwd_natural(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr,
+                                lse_ptr, stream)
 
 
 def moda_bwd(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes, out_ptr,
@@ -236,6 +243,23 @@ def depth_forward(q, kd, vd, *, with_lse: bool = False):
     shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     packed = pack_depth_cache(kd, vd, shape)
     return depth_fwd(q, packed, Hkv, L, with_lse=with_lse)
+
+
+def fwd_natural(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=None):
+    """MoDA forward straight from the natural depth layout (no repack)."""
+    import torch
+    _check_tensors(q, k, v, kd, vd)
+    B, Hq, T, d = q.shape
+    L = 0 if kd is None else kd.shape[3]
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(moda_fwd_natural(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None),
+                            _ptr(vd if L else None), _ptr(out), _ptr(lse), _stream_ptr(q)),
+           "moda_fwd_natural")
+    return (out, lse) if with_lse else out
 
 
 def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, delta=None):

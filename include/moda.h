@@ -110,6 +110,22 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k,
                             const void *v, void *out, float *lse,
                             void *hip_stream);
 
+/* MoDA forward reading the depth keys and values in their natural layout
+ * [B, Hkv, T, L, d] instead of the packed cache: the same result as
+ * moda_fwd (bit for bit), without a repack.  It measures whether the packed
+ * layout earns its repack (the hyper.ai page on arXiv 2603.15619, section
+ * "Hardware-efficient implementation", motivates its chunk- and group-aware
+ * depth layouts by the cost of non-contiguous depth reads).
+ *
+ *   q, k, v          : as for moda_fwd (read only)
+ *   k_depth, v_depth : depth K, V [B, Hkv, T, L, d] (read only; NULL if L == 0)
+ *   out, lse         : as for moda_fwd
+ * Supports bf16 with d = 128 and T * L below 2^23 (MODA_ERR_UNSUPPORTED
+ * otherwise).  Same validation, ownership and asynchrony rules as moda_fwd. */
+moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k,
+                             const void *v, const void *k_depth, const void *v_depth,
+                             void *out, float *lse, void *hip_stream);
+
 /* Depth attention alone: each query row (b, h, t) attends over its own
  * token's L depth entries only, under one softmax scaled by 1/sqrt(d), and
  * gets their weighted values.  No sequence key takes part.

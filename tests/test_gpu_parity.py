@@ -169,6 +169,26 @@ def test_rescale_paths(m, dev, kind, Hq, Hkv):
     assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
 
 
+# ------------------------------------------------------------------ natural depth layout
+
+NATURAL_SHAPES = [(1, 16, 4, 70, 5), (2, 4, 4, 9, 33), (1, 8, 1, 40, 65), (1, 32, 8, 300, 128),
+                  (1, 6, 2, 257, 3), (1, 16, 4, 1000, 24)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
+def test_fwd_natural_matches_packed(m, dev, B, Hq, Hkv, T, L):
+    """moda_fwd_natural (depth K/V read in their natural layout) gives the
+    packed path's O and LSE bit for bit: same operands, same MFMA order."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=700 + T + L)
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, L)
+    out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                 with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
+
+
 # ------------------------------------------------------------------ depth attention alone
 
 DEPTH_SHAPES = [  # (B, Hq, Hkv, T, L, d, dtype): MFMA path and generic path, ragged sizes
