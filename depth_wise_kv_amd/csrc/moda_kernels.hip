@@ -83,74 +83,6 @@ __device__ unsigned long long moda_trace_buf[16];
   } while (0)
 #endif
 
-struct MfmaState {
-  float m;          // reference max of scaled logits (log2 units)
-  float lsum;       // this lane's partial sum of 2^(x - m)
-  floatx16 acc[4];  // O^T accumulator: 4 blocks of 32 head-dim rows
-};
-
-// Weights 2^(s * scale_log2 - m) of NB score blocks as bf16 B operands,
-// pb[2*i + {0,1}] for block i, and their sum (this lane's share of the row).
-template <int NB>
-__device__ __forceinline__ float tile_weights(const floatx16 *s, float scale_log2, float neg_m,
-                                              bf16x8 *pb) {
-  float sum = 0.f;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    u32x4 w[2];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = fast_exp2(fmaf(s[b][r], scale_log2, neg_m));
-      const float p1 = fast_exp2(fmaf(s[b][r + 1], scale_log2, neg_m));
-      sum += p0 + p1;
-      w[r >> 3][(r & 7) >> 1] = cvt_bf16x2(p0, p1);
-    }
-    pb[2 * b] = __builtin_bit_cast(bf16x8, w[0]);
-    pb[2 * b + 1] = __builtin_bit_cast(bf16x8, w[1]);
-  }
-  return sum;
-}
-
-// A row's weights in one tile may sum to at most this much before the row
-// moves its reference max; every weight stays <= 2^12.
-constexpr float TILE_SUM_LIMIT = 4096.0f;
-
-// Online-softmax update for NB score blocks of 32 entries each (already
-// masked with -inf): turn scores into weights against the row's reference
-// max and return them as bf16 B operands, pb[2*i + {0,1}] for block i.
-// The weights are first taken against the current reference.  A row with no
-// reference yet, or whose weights in this tile sum past TILE_SUM_LIMIT, moves
-// its reference to the tile's max, rescales its state and takes its weights
-// again.  The branch is wave-wide, but each row decides from its own scores and
-// a row that does not move recomputes exactly the same weights, so a row's
-// result never depends on the other rows of the wave.
-template <int NB>
-__device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s, float scale_log2,
-                                               bf16x8 *pb) {
-  const bool fresh = st.m == -INFINITY;
-  float sum = tile_weights<NB>(s, scale_log2, fresh ? 0.f : -st.m, pb);
-  const bool need = fresh || !(pair_sum(sum) <= TILE_SUM_LIMIT);
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    const float mt = pair_max(mx) * scale_log2;
-    const float m_new = need ? fmaxf(mt, st.m) : st.m;
-    const float alpha = m_new == st.m ? 1.0f : fast_exp2(st.m - m_new);
-    st.m = m_new;
-    st.lsum *= alpha;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
-    // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
-    sum = tile_weights<NB>(s, scale_log2, st.m == -INFINITY ? 0.f : -st.m, pb);
-  }
-  st.lsum += sum;
-}
-
 // ---------------------------------------------------------------------------
 // Fused forward, MFMA path.
 //
