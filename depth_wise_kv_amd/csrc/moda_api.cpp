@@ -139,6 +139,41 @@ moda_status check_qkvo(const void *q, const void *k, const void *v, const void *
   return MODA_OK;
 }
 
+// Decode split: about kDecodeGroups workgroups in all (two per compute unit),
+// each cache chunk a multiple of the 8 waves x 32 entries one pass covers.
+constexpr int64_t kDecodeGroups = 512;
+constexpr int64_t kDecodeChunkStep = 256;
+
+struct DecodePlan {
+  int64_t chunk, nsplit, nparts;
+};
+
+DecodePlan decode_plan(const moda_shape *s) {
+  const int64_t BH = s->B * s->Hkv;
+  const int64_t want = (kDecodeGroups + BH - 1) / BH;
+  int64_t chunk = (s->T + want - 1) / want;
+  chunk = (chunk + kDecodeChunkStep - 1) / kDecodeChunkStep * kDecodeChunkStep;
+  DecodePlan pl;
+  pl.chunk = chunk;
+  pl.nsplit = (s->T + chunk - 1) / chunk;
+  pl.nparts = pl.nsplit + (s->L > 0 ? 1 : 0);
+  return pl;
+}
+
+moda_status check_decode_shape(const moda_shape *s) {
+  moda_status st = check_shape_impl(s);
+  if (st != MODA_OK) return st;
+  if (!use_mfma(s)) return fail(MODA_ERR_UNSUPPORTED, "moda_decode supports bf16 with d = 128");
+  if (s->Hq / s->Hkv > 32) return fail(MODA_ERR_UNSUPPORTED, "moda_decode supports G up to 32");
+  if (s->L >= ((int64_t)1 << 23)) return fail(MODA_ERR_UNSUPPORTED, "moda_decode supports L below 2^23");
+  if (s->B * s->Hkv > 65535) return fail(MODA_ERR_UNSUPPORTED, "B * Hkv above 65535");
+  return MODA_OK;
+}
+
+size_t decode_ws_bytes(const moda_shape *s) {
+  return (size_t)(s->B * s->Hq * decode_plan(s).nparts * moda::kDecodeRecord * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,6 +353,54 @@ moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k, 
   a.vd_nat = v_depth;
   return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), (hipStream_t)hip_stream),
                     "fwd launch");
+}
+
+size_t moda_decode_workspace_bytes(const moda_shape *s) {
+  if (check_decode_shape(s) != MODA_OK) return 0;
+  return decode_ws_bytes(s);
+}
+
+moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
+                        const void *v_cache, const void *k_depth, const void *v_depth, void *out,
+                        float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  moda_status st = check_decode_shape(s);
+  if (st != MODA_OK) return st;
+  st = check_qkvo(q, k_cache, v_cache, out, lse);
+  if (st != MODA_OK) return st;
+  if (s->L > 0) {
+    if (!k_depth || !v_depth)
+      return fail(MODA_ERR_INVALID_ARG, "k_depth and v_depth must be non-NULL when L > 0");
+    if (!aligned16(k_depth) || !aligned16(v_depth))
+      return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  } else if (k_depth || v_depth) {
+    return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
+  }
+  if (!workspace || !aligned16(workspace))
+    return fail(MODA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
+  const size_t need = decode_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+  const DecodePlan pl = decode_plan(s);
+  moda::DecArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kd = k_depth;
+  a.vd = v_depth;
+  a.out = out;
+  a.lse = lse;
+  a.ws = (float *)workspace;
+  a.B = s->B;
+  a.Hq = s->Hq;
+  a.Hkv = s->Hkv;
+  a.T = s->T;
+  a.L = s->L;
+  a.chunk = pl.chunk;
+  a.nsplit = pl.nsplit;
+  a.nparts = pl.nparts;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
+  return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
 }
 
 const char *moda_status_string(moda_status st) {

@@ -1,0 +1,255 @@
+// HIP kernels of the MoDA decode step for gfx950 (MI355X): bf16, head dim 128.
+//
+// One new token per sequence: its G query heads per KV head attend, under
+// one softmax scaled by 1/sqrt(d), over the whole KV cache (every cached key
+// is at or before the new token) and over the new token's own L depth
+// entries (hyper.ai page on arXiv 2603.15619, section "Mixture-of-Depths
+// Attention (MoDA)").  This is the last query row of the forward.
+//
+// The cache is read once, split over many workgroups for bandwidth:
+//   moda_decode_part   a workgroup takes one part of one (b, kv head)'s
+//                      entries: a chunk of the cache, or the depth entries.
+//                      Each of its 8 waves walks every 8th 32-entry block of
+//                      the part; the waves then merge their softmax states
+//                      through LDS and the workgroup leaves one partial state
+//                      (unnormalised O, reference max, weight sum) per row.
+//   moda_decode_merge  merges the partial states of each query row and
+//                      normalises once.
+// Per block: K rows straight into MFMA operand registers (16 bytes of a row
+// per lane, the next block's already in flight), V rows into the wave's
+// 8 KiB of LDS, column-swizzled, read transposed; S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with a lane owning a query row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moda_device.h"
+#include "moda_internal.h"
+
+namespace moda {
+
+constexpr int DEC_WAVES = 8;
+constexpr int DEC_D = kMfmaD;  // 128
+constexpr int MERGE_WAVES = 16;
+constexpr int MERGE_UNROLL = 8;
+
+__global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
+  __shared__ __attribute__((aligned(1024))) char slots[DEC_WAVES][32 * 256];
+  __shared__ float m_s[DEC_WAVES][32], l_s[DEC_WAVES][32];
+  const int G = (int)(p.Hq / p.Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5;
+  const TileFrags fr(lane);
+
+  const int64_t BH = p.B * p.Hkv;
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t part = blockIdx.x / BH;  // 0 .. nsplit-1: cache chunks; nsplit: depth entries
+  const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+
+  // this lane's query row: head hkv*G + li (lanes past G compute on zeros)
+  const bool row_ok = li < G;
+  const int64_t qrow = b * p.Hq + hkv * G + (row_ok ? li : 0);
+  bf16x8 qb[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 u = row_ok ? *(const u32x4 *)((const __bf16 *)p.q + qrow * DEC_D + 64 * lh + 8 * ks)
+                           : u32x4{0, 0, 0, 0};
+    qb[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+
+  // the part's entries [e_lo, e_hi) of a source of n_src rows
+  const bool depth = part == p.nsplit;
+  const int64_t n_src = depth ? p.L : p.T;
+  const int64_t e_lo = depth ? 0 : part * p.chunk;
+  int64_t e_hi = depth ? p.L : e_lo + p.chunk;
+  if (e_hi > n_src) e_hi = n_src;
+  const __bf16 *ksrc = (const __bf16 *)(depth ? p.kd : p.k) + bh * n_src * DEC_D;
+  const char *vsrc = (const char *)(depth ? p.vd : p.v) + bh * n_src * (DEC_D * 2);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)vsrc, (short)0, (int)(n_src * (DEC_D * 2)), 0x00020000);
+  char *const slot = slots[wave];
+
+  MfmaState st;
+  st.m = -INFINITY;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] = 0.f;
+
+  auto load_k = [&](int64_t e0, u32x4 (&kd)[8]) {
+    const int64_t e = e0 + li;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kd[ks] = e < n_src ? *(const u32x4 *)(ksrc + e * DEC_D + 64 * lh + 8 * ks)
+                         : u32x4{0, 0, 0, 0};
+  };
+  const int64_t n_blk = (e_hi - e_lo + 31) / 32;
+  u32x4 kd[8];
+  if (wave < n_blk) load_k(e_lo + 32 * wave, kd);
+  for (int64_t i = wave; i < n_blk; i += DEC_WAVES) {
+    const int64_t e0 = e_lo + 32 * i;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
+    // V rows e0 .. e0+31 into the slot, column-swizzled (rows past the source read as zeros)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + (lane >> 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (__attribute__((address_space(3))) void *)(slot + 4 * j * 256), 16,
+          (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3)))), (uint32_t)(e0 * 256), 0,
+          0);
+    }
+    floatx16 sd[1];
+    floatx16 sd2[2] = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sd2[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]),
+                                                            qb[ks], sd2[ks & 1], 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
+    const bool more = i + DEC_WAVES < n_blk;
+    if (more) load_k(e0 + 32 * DEC_WAVES, kd);
+    // register rr holds entry e0 + 8*(rr/4) + 4*lh + rr%4: entries past the part drop out
+    const int64_t lim64 = e_hi - e0 - 4 * lh;
+    const int lim = (int)(lim64 > 64 ? 64 : lim64);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      if (8 * (rr >> 2) + (rr & 3) >= lim) sd[0][rr] = -INFINITY;
+    bf16x8 pb[2];
+    softmax_update<1>(st, sd, p.scale_log2, pb);
+    // the V rows have landed (the next block's K loads may still be in flight)
+    if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else wait_vmem();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb + kk),
+                                                             pb[kk], st.acc[nb], 0, 0, 0);
+  }
+
+  // Merge the 8 waves' states: a common reference max per row, then the
+  // rescaled accumulators summed pairwise through LDS (the V slots, now free).
+  if (lh == 0) m_s[wave][li] = st.m;
+  __syncthreads();
+  float m_row = m_s[0][li];
+#pragma unroll
+  for (int w = 1; w < DEC_WAVES; ++w) m_row = fmaxf(m_row, m_s[w][li]);
+  const float alpha = st.m == -INFINITY ? 0.f : fast_exp2(st.m - m_row);
+  const float l_wave = pair_sum(st.lsum) * alpha;
+  if (lh == 0) l_s[wave][li] = l_wave;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] *= alpha;
+  float *const red = (float *)&slots[0][0];  // 4 regions of 64 registers x 64 lanes
+#pragma unroll
+  for (int step = DEC_WAVES / 2; step >= 1; step >>= 1) {
+    if (wave >= step && wave < 2 * step) {
+      float *r = red + (wave - step) * 4096 + lane;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) r[(16 * nb + rr) * 64] = st.acc[nb][rr];
+    }
+    __syncthreads();
+    if (wave < step) {
+      const float *r = red + wave * 4096 + lane;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] += r[(16 * nb + rr) * 64];
+    }
+    __syncthreads();
+  }
+
+  // wave 0 writes the workgroup's state of each row: O (unnormalised), max, sum
+  if (wave == 0 && row_ok) {
+    float *rec = p.ws + (qrow * p.nparts + part) * kDecodeRecord;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4 *)(rec + 32 * nb + 8 * q4 + 4 * lh) =
+            make_float4(st.acc[nb][4 * q4], st.acc[nb][4 * q4 + 1], st.acc[nb][4 * q4 + 2],
+                        st.acc[nb][4 * q4 + 3]);
+    if (lh == 0) {
+      float l_row = 0.f;
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) l_row += l_s[w][li];
+      rec[DEC_D] = m_row;
+      rec[DEC_D + 1] = l_row;
+    }
+  }
+}
+
+// One workgroup per query row: each wave folds every 16th partial state into
+// a running (max, sum, O), the 16 wave states merge in LDS, one normalisation.
+__global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p) {
+  __shared__ float o_s[MERGE_WAVES][DEC_D];
+  __shared__ float m_s[MERGE_WAVES], l_s[MERGE_WAVES];
+  const int64_t row = blockIdx.x;  // b * Hq + head
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t n = p.nparts;
+  const float *rec = p.ws + row * n * kDecodeRecord;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int64_t base = wave; base < n; base += MERGE_WAVES * MERGE_UNROLL) {
+    float mi[MERGE_UNROLL], li[MERGE_UNROLL];
+    float2 oi[MERGE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u) {
+      const int64_t idx = base + MERGE_WAVES * u;
+      const float *r = rec + (idx < n ? idx : 0) * kDecodeRecord;
+      mi[u] = idx < n ? r[DEC_D] : -INFINITY;
+      li[u] = r[DEC_D + 1];
+      oi[u] = *(const float2 *)(r + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u) {
+      if (mi[u] == -INFINITY) continue;  // past the end, or a state with no entry
+      const float m_new = fmaxf(m, mi[u]);
+      const float a = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+      const float c = fast_exp2(mi[u] - m_new);
+      l = l * a + li[u] * c;
+      o0 = o0 * a + oi[u].x * c;
+      o1 = o1 * a + oi[u].y * c;
+      m = m_new;
+    }
+  }
+  if (lane == 0) {
+    m_s[wave] = m;
+    l_s[wave] = l;
+  }
+  o_s[wave][2 * lane] = o0;
+  o_s[wave][2 * lane + 1] = o1;
+  __syncthreads();
+  if (wave != 0) return;
+  float M = m_s[0];
+#pragma unroll
+  for (int w = 1; w < MERGE_WAVES; ++w) M = fmaxf(M, m_s[w]);
+  float L = 0.f, O0 = 0.f, O1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < MERGE_WAVES; ++w) {
+    if (m_s[w] == -INFINITY) continue;
+    const float c = fast_exp2(m_s[w] - M);
+    L += l_s[w] * c;
+    O0 += o_s[w][2 * lane] * c;
+    O1 += o_s[w][2 * lane + 1] * c;
+  }
+  const float inv = 1.0f / L;
+  *(uint32_t *)((__bf16 *)p.out + row * DEC_D + 2 * lane) = cvt_bf16x2(O0 * inv, O1 * inv);
+  if (p.lse && lane == 0) p.lse[row] = (M + __log2f(L)) * 0.69314718055994531f;
+}
+
+hipError_t launch_decode(const DecArgs &a, hipStream_t s) {
+  const int64_t BH = a.B * a.Hkv;
+  hipLaunchKernelGGL(moda_decode_part, dim3((uint32_t)(BH * a.nparts)), dim3(64 * DEC_WAVES), 0,
+                     s, a);
+  hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moda

@@ -42,6 +42,23 @@ struct BwdArgs {
   float scale;       // 1 / sqrt(d)
 };
 
+// Decode step: one query row per (b, head) over a KV cache of T entries and
+// the new token's L depth entries, split into nparts workgroup parts per
+// (b, kv head): nsplit cache chunks of `chunk` entries, then (if L > 0) one
+// part for the depth entries.  Each part leaves one record per query row in
+// ws: O (unnormalised, kMfmaD floats), reference max (log2 units), weight sum.
+constexpr int kDecodeRecord = kMfmaD + 4;  // floats per record (2 of padding)
+
+struct DecArgs {
+  const void *q, *k, *v, *kd, *vd;  // q [B,Hq,d]; k, v [B,Hkv,T,d]; kd, vd [B,Hkv,L,d]
+  void *out;                        // [B,Hq,d]
+  float *lse;                       // [B,Hq] or null
+  float *ws;                        // [B*Hq, nparts, kDecodeRecord]
+  int64_t B, Hq, Hkv, T, L;
+  int64_t chunk, nsplit, nparts;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
 struct PackArgs {
   const void *kd, *vd;
   void *packed;
@@ -55,6 +72,9 @@ hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
 
 // Backward, bf16, d == 128, G <= 64: delta, dQ, then dK/dV.
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
+
+// Decode step, bf16, d == 128, G <= 32: partial states, then their merge.
+hipError_t launch_decode(const DecArgs &a, hipStream_t s);
 
 // Generic path: fp32 or bf16, d in {32, 64, 128}, any G.
 hipError_t launch_fwd_generic(const FwdArgs &a, bool bf16, hipStream_t s);

@@ -24,6 +24,7 @@ MODA_F32, MODA_BF16 = 0, 1
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
+           "moda_decode_workspace_bytes", "moda_decode",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -62,6 +63,10 @@ def _load():
     lib.moda_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                              vp]
     lib.moda_bwd.restype = ctypes.c_int
+    lib.moda_decode_workspace_bytes.argtypes = [sp]
+    lib.moda_decode_workspace_bytes.restype = sz
+    lib.moda_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moda_decode.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     lib.moda_last_error.argtypes = []
@@ -135,6 +140,16 @@ def moda_bwd(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_byte
     return lib.moda_bwd(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes,
                         out_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dkd_ptr, dvd_ptr,
                         delta_ptr, stream)
+
+
+def moda_decode_workspace_bytes(shape: ModaShape) -> int:
+    return int(lib.moda_decode_workspace_bytes(_sref(shape)))
+
+
+def moda_decode(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, ws_ptr, ws_bytes,
+                stream):
+    return lib.moda_decode(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr,
+                           ws_ptr, ws_bytes, stream)
 
 
 def moda_status_string(status: int) -> str:
@@ -282,6 +297,32 @@ def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, d
                     _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
                     _ptr(dvd), _ptr(delta), _stream_ptr(q)), "moda_bwd")
     return grads
+
+
+def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=None,
+           workspace=None):
+    """Decode step: q [B,Hq,d] of the new token over the cache k, v [B,Hkv,T,d]
+    (the new token's own K, V last) and its depth entries kd, vd [B,Hkv,L,d].
+    ``workspace`` may pass a uint8 device tensor of at least
+    moda_decode_workspace_bytes bytes."""
+    import torch
+    _check_tensors(q, k, v, kd, vd)
+    B, Hq, d = q.shape
+    T = k.shape[2]
+    L = 0 if kd is None else kd.shape[2]
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    need = moda_decode_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(moda_decode(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None),
+                       _ptr(vd if L else None), _ptr(out), _ptr(lse), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream_ptr(q)),
+           "moda_decode")
+    return (out, lse) if with_lse else out
 
 
 def moda_forward(q, k, v, kd=None, vd=None, *, with_lse: bool = False):

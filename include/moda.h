@@ -170,6 +170,40 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
                      const void *dout, void *dq, void *dk, void *dv, void *dk_depth,
                      void *dv_depth, float *delta, void *hip_stream);
 
+/* Bytes of device workspace moda_decode needs for shape `s`; 0 if moda_decode
+ * does not accept `s`.  Host only. */
+size_t moda_decode_workspace_bytes(const moda_shape *s);
+
+/* MoDA decode step: the one new token of each sequence attends over the KV
+ * cache and over its own depth entries.  Row (b, h) takes one softmax, scaled
+ * by 1/sqrt(d), over the cache keys K[b, g, j, :] for j = 0..T-1 (the new
+ * token's own key is the last of them, so every cached key is causal) and the
+ * token's L depth keys Kd[b, g, i, :], with g = h / G; its output is the
+ * weight-averaged matching values.  This is the forward's row t = T-1
+ * (hyper.ai page on arXiv 2603.15619, section "Mixture-of-Depths Attention
+ * (MoDA)"), evaluated without the other rows.
+ *
+ * Shape: `s->T` is the cache length including the new token, `s->L` the
+ * number of the token's depth entries.
+ *   q                : Q [B, Hq, d] of the new token (read only)
+ *   k_cache, v_cache : K, V [B, Hkv, T, d] (read only)
+ *   k_depth, v_depth : the new token's depth K, V [B, Hkv, L, d] (read only;
+ *                      NULL if L == 0)
+ *   out              : O [B, Hq, d], written in full
+ *   lse              : NULL, or LSE [B, Hq] float32 (natural log)
+ *   workspace        : device scratch of workspace_bytes >=
+ *                      moda_decode_workspace_bytes(s) bytes, overwritten; its
+ *                      contents need no initialisation and mean nothing after
+ *                      the call.  Two calls that overlap in time must not share
+ *                      one workspace.
+ * Supports bf16 with d = 128, G = Hq / Hkv up to 32 and L below 2^23
+ * (MODA_ERR_UNSUPPORTED otherwise).  Same validation, ownership and
+ * asynchrony rules as moda_fwd. */
+moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
+                        const void *v_cache, const void *k_depth, const void *v_depth,
+                        void *out, float *lse, void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+
 /* Static text of a status code (never NULL). */
 const char *moda_status_string(moda_status st);
 

@@ -103,6 +103,35 @@ def test_fwd_rejects_before_launch(m):
     assert m.moda_depth_fwd(None, p, p, nb, p, None, None) == m.MODA_ERR_INVALID_ARG
 
 
+def test_decode_workspace_and_rejects(m):
+    """Decode: workspace size is a host-side function of the shape; argument
+    errors come back as statuses before any device call."""
+    s = shape(m, T=65536, L=32)
+    ws = m.moda_decode_workspace_bytes(s)
+    # one 132-float record per query row and workgroup part (cache chunks + depth)
+    assert ws > 0 and ws % (16 * 132 * 4) == 0
+    parts = ws // (16 * 132 * 4)
+    s0 = shape(m, T=65536, L=0)
+    assert m.moda_decode_workspace_bytes(s0) == 16 * (parts - 1) * 132 * 4
+    assert m.moda_decode_workspace_bytes(shape(m, dtype="f32")) == 0
+    assert m.moda_decode_workspace_bytes(shape(m, Hq=64, Hkv=1)) == 0   # G = 64
+    assert m.moda_decode_workspace_bytes(shape(m, Hq=32, Hkv=1)) > 0    # G = 32
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    ok = (p, p, p, p, p, p, None, p, ws, None)
+    assert m.moda_decode(None, *ok) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(shape(m, dtype="f32"), *ok) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_decode(shape(m, Hq=64, Hkv=1), *ok) == m.MODA_ERR_UNSUPPORTED
+    assert m.moda_decode(s, None, p, p, p, p, p, None, p, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s, p, p, p, None, p, p, None, p, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s0, p, p, p, p, p, p, None, p, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s, p, p, p, p, mis, p, None, p, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s, p, p, p, p, p, p, None, None, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s, p, p, p, p, p, p, None, mis, ws, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode(s, p, p, p, p, p, p, None, p, ws - 1, None) == m.MODA_ERR_INVALID_ARG
+    assert "too small" in m.moda_last_error()
+
+
 def test_binding_refuses_host_tensors(m):
     import torch
     q = torch.zeros(1, 2, 4, 32)

@@ -432,3 +432,77 @@ def test_bwd_layer_1p5b_full(m, dev):
         e = max_err(out_to_f64(g), r)
         print(f"[parity] bwd layer_1p5b {name} max|err|={e:.3e} max|ref|={scale:.3e}", flush=True)
         assert e <= BWD_TOL * scale
+
+
+# ------------------------------------------------------------------ decode step
+
+DECODE_SHAPES = [  # (B, Hq, Hkv, T, L): T = cache length with the new token; ragged, G 1..32
+    (1, 2, 1, 1, 0), (1, 4, 4, 1, 3), (2, 8, 2, 37, 5), (3, 8, 8, 1000, 1), (1, 32, 1, 300, 24),
+    (2, 12, 4, 2050, 33), (1, 2, 1, 513, 128), (1, 16, 4, 4096, 24), (1, 8, 2, 9000, 0),
+    (2, 4, 1, 257, 65),
+]
+
+
+def decode_case(cfg, dev):
+    """Decode inputs cut from a forward case: the last token's query and depth
+    rows, the whole K/V as the cache."""
+    d_in = device_case(cfg, dev)
+    T, L = cfg["T"], cfg["L"]
+    q = d_in["q"][:, :, T - 1].contiguous()
+    kd = d_in["kd"][:, :, T - 1].contiguous() if L else None
+    vd = d_in["vd"][:, :, T - 1].contiguous() if L else None
+    return d_in, q, kd, vd
+
+
+def decode_check(m, cfg, dev):
+    d_in, q, kd, vd = decode_case(cfg, dev)
+    out, lse = m.decode(q, d_in["k"], d_in["v"], kd, vd, with_lse=True)
+    torch.cuda.synchronize()
+    B, Hq, T = cfg["B"], cfg["Hq"], cfg["T"]
+    rows = np.array([(b, h, T - 1) for b in range(B) for h in range(Hq)], np.int64)
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    e_o = max_err(out_to_f64(out).reshape(B * Hq, -1), ref)
+    e_l = max_err(lse.cpu().numpy().reshape(-1), rlse)
+    print(f"[decode] {cfg.get('name', cfg)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    return d_in, q, kd, vd, out, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", DECODE_SHAPES,
+                         ids=[f"B{b}_Hq{h}_Hkv{k}_T{t}_L{l}" for b, h, k, t, l in DECODE_SHAPES])
+def test_decode_parity(m, dev, B, Hq, Hkv, T, L):
+    """The decode step against the oracle's row t = T-1 of every (b, head)."""
+    decode_check(m, shape_cfg(B, Hq, Hkv, T, L, seed=B * 1000 + T + L), dev)
+
+
+@pytest.mark.parametrize("name", ["long_64k", "depth_heavy"])
+def test_decode_full_size(m, dev, name):
+    """Decode over the full-size caches (64K entries; 8K entries x 32 heads)."""
+    decode_check(m, dict(WORKLOADS[name], name=name), dev)
+    torch.cuda.empty_cache()
+
+
+def test_decode_matches_forward_last_row(m, dev):
+    """Decode equals the forward's last query row up to summation order."""
+    cfg = shape_cfg(2, 16, 4, 3000, 24, scale=0.5, seed=77)
+    d_in, q, kd, vd, out, lse = decode_check(m, cfg, dev)
+    f_out, f_lse = run_full(m, d_in, cfg["L"])
+    e_o = (out.float() - f_out[:, :, -1].float()).abs().max().item()
+    e_l = (lse - f_lse[:, :, -1]).abs().max().item()
+    print(f"[decode] vs forward last row max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
+def test_decode_workspace_reuse(m, dev):
+    """One workspace serves calls of different shapes in a row; its contents
+    from an earlier call never leak into a later result."""
+    big = shape_cfg(1, 16, 4, 5000, 24, seed=91)
+    small = shape_cfg(1, 8, 2, 700, 3, seed=92)
+    sb = m.make_shape(1, 16, 4, 5000, 24, 128, "bf16")
+    ws = torch.full((m.moda_decode_workspace_bytes(sb),), 0x7F, dtype=torch.uint8, device=dev)
+    for cfg in (big, small, big):
+        d_in, q, kd, vd = decode_case(cfg, dev)
+        ref_out = m.decode(q, d_in["k"], d_in["v"], kd, vd)
+        out = m.decode(q, d_in["k"], d_in["v"], kd, vd, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
