@@ -6,10 +6,13 @@ HBM: moda_pack_depth_cache (depth repack) + moda_fwd (fused forward).  The
 causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
 MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
 same packed cache for its HBM rate, and the forward straight from the natural
-depth layout (moda_fwd_natural) for the repack ablation.  Prints one JSON line.
+depth layout (moda_fwd_natural) for the repack ablation, the decode step
+(moda_decode: the last token over the whole cache) for its HBM rate.  Prints
+one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
+    python bench.py --decode-sweep     # one JSON line per decode shape
 
 FLOP convention (algorithmic, per query head): 4 * d * (T(T+1)/2 + T*L), the
 diagonal counted, exponentials not counted.  The backward (moda_bwd, timed
@@ -62,6 +65,12 @@ def depth_bytes(c):
 def pack_bytes(c):
     """Depth K/V read once and written once."""
     return 2 * (2 * c["B"] * c["Hkv"] * c["T"] * c["L"] * c["d"] * es(c))
+
+
+def decode_bytes(c):
+    """Decode step: the KV cache and the new token's depth K/V once, q and O."""
+    B, Hq, Hkv, T, L, d = c["B"], c["Hq"], c["Hkv"], c["T"], c["L"], c["d"]
+    return es(c) * (2 * B * Hkv * T * d + 2 * B * Hkv * L * d + 2 * B * Hq * d)
 
 
 def roofline(c, fwd_ms, traffic):
@@ -153,6 +162,82 @@ def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
                       f"full workload extrapolated to {full_s:.0f} s"}
 
 
+def decode_inputs(cfg, d_in):
+    """Decode inputs cut from a forward case: the last token's query and depth
+    rows; the whole K/V is the cache."""
+    import torch
+    from depth_wise_kv_amd import moda
+    T, L = cfg["T"], cfg["L"]
+    q = d_in["q"][:, :, T - 1].contiguous()
+    kd = d_in["kd"][:, :, T - 1].contiguous() if L else None
+    vd = d_in["vd"][:, :, T - 1].contiguous() if L else None
+    shape = moda.make_shape(cfg["B"], cfg["Hq"], cfg["Hkv"], T, L, cfg["d"], cfg["dtype"])
+    ws = torch.empty(max(16, moda.moda_decode_workspace_bytes(shape)), dtype=torch.uint8,
+                     device=q.device)
+    return q, kd, vd, ws
+
+
+def time_decode(cfg, d_in, steps, stream, reps=20, given=None):
+    """Mean duration of one decode call (both of its kernels), over steps*reps
+    calls replayed from a graph."""
+    import torch
+    from depth_wise_kv_amd import moda
+    if given is None:
+        q, kd, vd, ws = decode_inputs(cfg, d_in)
+    else:
+        q, kd, vd = given
+        shape = moda.make_shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["L"], cfg["d"],
+                                cfg["dtype"])
+        ws = torch.empty(max(16, moda.moda_decode_workspace_bytes(shape)), dtype=torch.uint8,
+                         device=q.device)
+    out = torch.empty_like(q)
+
+    def dec():
+        for _ in range(reps):
+            moda.decode(q, d_in["k"], d_in["v"], kd, vd, out=out, workspace=ws)
+
+    # replayed from a HIP graph, so the host's per-call launch cost (tens of
+    # microseconds through Python) does not hide the device time
+    dec()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dec()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = float(np.mean(timed(graph.replay, steps, stream))) / reps
+    del graph
+    return ms
+
+
+# Decode shapes (B, Hq, Hkv, T, L): the forward workloads' heads and lengths,
+# plus serving batches of many sequences.
+DECODE_SWEEP = [(1, 16, 4, 65536, 32), (4, 32, 8, 8192, 128), (2, 16, 4, 4096, 24),
+                (1, 16, 4, 4096, 24), (32, 16, 4, 8192, 24), (64, 16, 4, 4096, 24),
+                (8, 32, 8, 32768, 64), (16, 16, 16, 16384, 32)]
+
+
+def decode_sweep(steps):
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(6000)
+    for B, Hq, Hkv, T, L in DECODE_SWEEP:
+        c = dict(B=B, Hq=Hq, Hkv=Hkv, T=T, L=L, d=128, dtype="bf16")
+        r = lambda *sh: torch.randn(*sh, generator=g, device=dev).to(torch.bfloat16)
+        d_in = {"q": None, "k": r(B, Hkv, T, 128), "v": r(B, Hkv, T, 128)}
+        q = r(B, Hq, 128)
+        kd, vd = (r(B, Hkv, L, 128), r(B, Hkv, L, 128)) if L else (None, None)
+        ms = time_decode(c, d_in, steps, stream, given=(q, kd, vd))
+        print(json.dumps({"decode": f"B{B}_Hq{Hq}_Hkv{Hkv}_T{T}_L{L}", "us": ms * 1e3,
+                          "hbm_gbs": decode_bytes(c) / ms / 1e6,
+                          "pct_hbm_peak": 100.0 * decode_bytes(c) / ms / 1e6 / PEAK_HBM_GBS}),
+              flush=True)
+        del d_in, q, kd, vd
+        torch.cuda.empty_cache()
+
+
 def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
     import torch
     from depth_wise_kv_amd import moda
@@ -209,6 +294,9 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout)
         depth_ms = float(np.mean(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
                                        steps, stream)))
+    decode_ms = None
+    if cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["Hq"] // cfg["Hkv"] <= 32:
+        decode_ms = time_decode(cfg, d_in, steps, stream)
     bwd_ms = None
     if with_bwd and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["Hq"] // cfg["Hkv"] <= 32:
         # backward of the same step: O, LSE from the forward, a seeded dO
@@ -228,7 +316,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
         del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
-               depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms)
+               depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -251,6 +339,9 @@ def profile_only(cfg, which, steps):
         o_b, lse_b = moda.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
         dout = torch.randn_like(d_in["q"], dtype=torch.float32).to(d_in["q"].dtype)
         kd, vd = (d_in["kd"], d_in["vd"]) if L else (None, None)
+    if which == "decode":
+        dq, dkd, dvd, dws = decode_inputs(cfg, d_in)
+        dout_ = torch.empty_like(dq)
     torch.cuda.synchronize()
     for _ in range(steps):
         if which == "fwd":
@@ -259,6 +350,8 @@ def profile_only(cfg, which, steps):
             moda.causal_fwd(d_in["q"], d_in["k"], d_in["v"], out=out)
         elif which == "depth":
             moda.depth_fwd(d_in["q"], packed, cfg["Hkv"], L, out=out)
+        elif which == "decode":
+            moda.decode(dq, d_in["k"], d_in["v"], dkd, dvd, out=dout_, workspace=dws)
         elif which == "bwd":
             moda.bwd(d_in["q"], d_in["k"], d_in["v"], o_b, lse_b, dout, kd, vd, packed)
         else:
@@ -275,9 +368,11 @@ def main():
     ap.add_argument("--config", default="long_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="time the decode step on the decode shapes (one JSON line each)")
     ap.add_argument("--only", default=None,
                     help="with --sweep: run only points whose name contains this string")
-    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd"],
+    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd", "decode"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
                     help="time a bf16 N x N x N torch.matmul (hipBLASLt): the practical "
@@ -340,6 +435,9 @@ def main():
         profile_only(dict(named[args.config]), args.profile_kernel, args.steps)
         return
 
+    if args.decode_sweep:
+        decode_sweep(args.steps)
+        return
     if args.sweep:
         for c in sweep_points():
             if args.only and args.only not in c["name"]:
@@ -355,7 +453,10 @@ def main():
                               "fwd_natural_layout_ms": r["natural_ms"],
                               "depth_only_ms": r["depth_ms"],
                               "depth_only_hbm_gbs": (depth_bytes(c) / r["depth_ms"] / 1e6
-                                                     if r["depth_ms"] else None)}), flush=True)
+                                                     if r["depth_ms"] else None),
+                              "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,
+                              "decode_hbm_gbs": (decode_bytes(c) / r["decode_ms"] / 1e6
+                                                 if r["decode_ms"] else None)}), flush=True)
         return
 
     cfg = dict(named[args.config])
@@ -396,6 +497,8 @@ def main():
         "fwd_natural_layout_ms": r["natural_ms"],
         "bwd_ms": r["bwd_ms"],
         "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
+        "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,
+        "decode_hbm_gbs": decode_bytes(cfg) / r["decode_ms"] / 1e6 if r["decode_ms"] else None,
         "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:

@@ -139,25 +139,19 @@ moda_status check_qkvo(const void *q, const void *k, const void *v, const void *
   return MODA_OK;
 }
 
-// Decode split: about kDecodeGroups workgroups in all (two per compute unit),
-// each cache chunk a multiple of the 8 waves x 32 entries one pass covers.
-constexpr int64_t kDecodeGroups = 512;
-constexpr int64_t kDecodeChunkStep = 256;
+// Decode split: per (b, kv head) the cache's and the depth entries' 32-entry
+// blocks form one list, cut into nsplit even parts, one workgroup each.  The
+// parts fill the chip once (one 8-wave workgroup per compute unit, 256 units)
+// while every wave still gets a block.
+constexpr int64_t kDecodeGroups = 256;
+constexpr int64_t kDecodeWaves = 8;
 
-struct DecodePlan {
-  int64_t chunk, nsplit, nparts;
-};
-
-DecodePlan decode_plan(const moda_shape *s) {
+int64_t decode_splits(const moda_shape *s) {
   const int64_t BH = s->B * s->Hkv;
-  const int64_t want = (kDecodeGroups + BH - 1) / BH;
-  int64_t chunk = (s->T + want - 1) / want;
-  chunk = (chunk + kDecodeChunkStep - 1) / kDecodeChunkStep * kDecodeChunkStep;
-  DecodePlan pl;
-  pl.chunk = chunk;
-  pl.nsplit = (s->T + chunk - 1) / chunk;
-  pl.nparts = pl.nsplit + (s->L > 0 ? 1 : 0);
-  return pl;
+  const int64_t nb = (s->T + 31) / 32 + (s->L + 31) / 32;
+  int64_t n = kDecodeGroups / BH;
+  if (n > nb / kDecodeWaves) n = nb / kDecodeWaves;
+  return n < 1 ? 1 : n;
 }
 
 moda_status check_decode_shape(const moda_shape *s) {
@@ -171,7 +165,7 @@ moda_status check_decode_shape(const moda_shape *s) {
 }
 
 size_t decode_ws_bytes(const moda_shape *s) {
-  return (size_t)(s->B * s->Hq * decode_plan(s).nparts * moda::kDecodeRecord * 4);
+  return (size_t)(s->B * s->Hq * decode_splits(s) * moda::kDecodeRecord * 4);
 }
 
 }  // namespace
@@ -381,7 +375,6 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
   if (workspace_bytes < need)
     return fail(MODA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need) +
                                           " bytes, got " + std::to_string(workspace_bytes));
-  const DecodePlan pl = decode_plan(s);
   moda::DecArgs a{};
   a.q = q;
   a.k = k_cache;
@@ -396,9 +389,7 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
   a.Hkv = s->Hkv;
   a.T = s->T;
   a.L = s->L;
-  a.chunk = pl.chunk;
-  a.nsplit = pl.nsplit;
-  a.nparts = pl.nparts;
+  a.nsplit = decode_splits(s);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
   return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
 }

@@ -8,9 +8,10 @@
 //
 // The cache is read once, split over many workgroups for bandwidth:
 //   moda_decode_part   a workgroup takes one part of one (b, kv head)'s
-//                      entries: a chunk of the cache, or the depth entries.
-//                      Each of its 8 waves walks every 8th 32-entry block of
-//                      the part; the waves then merge their softmax states
+//                      entries (the cache's, then the depth entries, as one
+//                      list of 32-entry blocks split into nsplit even parts).
+//                      Each of its 8 waves walks every 8th block of the
+//                      part; the waves then merge their softmax states
 //                      through LDS and the workgroup leaves one partial state
 //                      (unnormalised O, reference max, weight sum) per row.
 //   moda_decode_merge  merges the partial states of each query row and
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
 
   const int64_t BH = p.B * p.Hkv;
   const int64_t bh = blockIdx.x % BH;
-  const int64_t part = blockIdx.x / BH;  // 0 .. nsplit-1: cache chunks; nsplit: depth entries
+  const int64_t part = blockIdx.x / BH;
   const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
 
   // this lane's query row: head hkv*G + li (lanes past G compute on zeros)
@@ -58,48 +59,58 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
     qb[ks] = __builtin_bit_cast(bf16x8, u);
   }
 
-  // the part's entries [e_lo, e_hi) of a source of n_src rows
-  const bool depth = part == p.nsplit;
-  const int64_t n_src = depth ? p.L : p.T;
-  const int64_t e_lo = depth ? 0 : part * p.chunk;
-  int64_t e_hi = depth ? p.L : e_lo + p.chunk;
-  if (e_hi > n_src) e_hi = n_src;
-  const __bf16 *ksrc = (const __bf16 *)(depth ? p.kd : p.k) + bh * n_src * DEC_D;
-  const char *vsrc = (const char *)(depth ? p.vd : p.v) + bh * n_src * (DEC_D * 2);
-  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)vsrc, (short)0, (int)(n_src * (DEC_D * 2)), 0x00020000);
+  // The (b, kv head)'s entries as one list of 32-entry blocks: the cache's
+  // nbc blocks, then the depth entries' blocks.  This part takes blocks
+  // [j_lo, j_hi) of it; wave w takes every DEC_WAVES-th of those from j_lo + w.
+  const int64_t nbc = (p.T + 31) / 32;
+  const int64_t nb = nbc + (p.L + 31) / 32;
+  const int64_t j_lo = part * nb / p.nsplit, j_hi = (part + 1) * nb / p.nsplit;
+  const __bf16 *kc = (const __bf16 *)p.k + bh * p.T * DEC_D;
+  const __bf16 *kdp = (const __bf16 *)p.kd + bh * p.L * DEC_D;
+  const __amdgpu_buffer_rsrc_t vc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.v + bh * p.T * (DEC_D * 2)), (short)0, (int)(p.T * (DEC_D * 2)),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t vd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const char *)p.vd + bh * p.L * (DEC_D * 2)), (short)0, (int)(p.L * (DEC_D * 2)),
+      0x00020000);
   char *const slot = slots[wave];
 
   MfmaState st;
   st.m = -INFINITY;
   st.lsum = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb4 = 0; nb4 < 4; ++nb4)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] = 0.f;
+    for (int rr = 0; rr < 16; ++rr) st.acc[nb4][rr] = 0.f;
 
-  auto load_k = [&](int64_t e0, u32x4 (&kd)[8]) {
-    const int64_t e = e0 + li;
+  // K rows of block j as MFMA A operands: entry 32*j' + li of its source, dims 64*lh + 8*ks
+  auto load_k = [&](int64_t j, u32x4 (&kd)[8]) {
+    const bool dep = j >= nbc;
+    const int64_t e = (dep ? j - nbc : j) * 32 + li;
+    const int64_t n = dep ? p.L : p.T;
+    const __bf16 *src = (dep ? kdp : kc) + e * DEC_D + 64 * lh;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      kd[ks] = e < n_src ? *(const u32x4 *)(ksrc + e * DEC_D + 64 * lh + 8 * ks)
-                         : u32x4{0, 0, 0, 0};
+      kd[ks] = e < n ? *(const u32x4 *)(src + 8 * ks) : u32x4{0, 0, 0, 0};
   };
-  const int64_t n_blk = (e_hi - e_lo + 31) / 32;
   u32x4 kd[8];
-  if (wave < n_blk) load_k(e_lo + 32 * wave, kd);
-  for (int64_t i = wave; i < n_blk; i += DEC_WAVES) {
-    const int64_t e0 = e_lo + 32 * i;
+  if (j_lo + wave < j_hi) load_k(j_lo + wave, kd);
+  for (int64_t j = j_lo + wave; j < j_hi; j += DEC_WAVES) {
+    const bool dep = j >= nbc;
+    const int64_t e0 = (dep ? j - nbc : j) * 32;
+    const int64_t n = dep ? p.L : p.T;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
     // V rows e0 .. e0+31 into the slot, column-swizzled (rows past the source read as zeros)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 4 * j + (lane >> 4);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 4 * i + (lane >> 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          v_rsrc, (__attribute__((address_space(3))) void *)(slot + 4 * j * 256), 16,
-          (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3)))), (uint32_t)(e0 * 256), 0,
-          0);
+          dep ? vd_rsrc : vc_rsrc, (__attribute__((address_space(3))) void *)(slot + 4 * i * 256),
+          16, (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3)))), (uint32_t)(e0 * 256),
+          0, 0);
     }
+    // every V load is issued before the first MFMA waits for its K operands
+    __builtin_amdgcn_sched_barrier(0);
     floatx16 sd[1];
     floatx16 sd2[2] = {};
 #pragma unroll
@@ -108,10 +119,10 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
                                                             qb[ks], sd2[ks & 1], 0, 0, 0);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
-    const bool more = i + DEC_WAVES < n_blk;
-    if (more) load_k(e0 + 32 * DEC_WAVES, kd);
-    // register rr holds entry e0 + 8*(rr/4) + 4*lh + rr%4: entries past the part drop out
-    const int64_t lim64 = e_hi - e0 - 4 * lh;
+    const bool more = j + DEC_WAVES < j_hi;
+    if (more) load_k(j + DEC_WAVES, kd);
+    // register rr holds entry e0 + 8*(rr/4) + 4*lh + rr%4: entries past the source drop out
+    const int64_t lim64 = n - e0 - 4 * lh;
     const int lim = (int)(lim64 > 64 ? 64 : lim64);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
@@ -124,9 +135,9 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb + kk),
-                                                             pb[kk], st.acc[nb], 0, 0, 0);
+      for (int nb4 = 0; nb4 < 4; ++nb4)
+        st.acc[nb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb4 + kk),
+                                                              pb[kk], st.acc[nb4], 0, 0, 0);
   }
 
   // Merge the 8 waves' states: a common reference max per row, then the
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
 
   // wave 0 writes the workgroup's state of each row: O (unnormalised), max, sum
   if (wave == 0 && row_ok) {
-    float *rec = p.ws + (qrow * p.nparts + part) * kDecodeRecord;
+    float *rec = p.ws + (qrow * p.nsplit + part) * kDecodeRecord;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p)
   const int64_t row = blockIdx.x;  // b * Hq + head
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t n = p.nparts;
+  const int64_t n = p.nsplit;
   const float *rec = p.ws + row * n * kDecodeRecord;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int64_t base = wave; base < n; base += MERGE_WAVES * MERGE_UNROLL) {
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p)
 
 hipError_t launch_decode(const DecArgs &a, hipStream_t s) {
   const int64_t BH = a.B * a.Hkv;
-  hipLaunchKernelGGL(moda_decode_part, dim3((uint32_t)(BH * a.nparts)), dim3(64 * DEC_WAVES), 0,
+  hipLaunchKernelGGL(moda_decode_part, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * DEC_WAVES), 0,
                      s, a);
   hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,
                      s, a);

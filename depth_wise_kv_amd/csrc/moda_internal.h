@@ -43,19 +43,19 @@ struct BwdArgs {
 };
 
 // Decode step: one query row per (b, head) over a KV cache of T entries and
-// the new token's L depth entries, split into nparts workgroup parts per
-// (b, kv head): nsplit cache chunks of `chunk` entries, then (if L > 0) one
-// part for the depth entries.  Each part leaves one record per query row in
-// ws: O (unnormalised, kMfmaD floats), reference max (log2 units), weight sum.
+// the new token's L depth entries.  Per (b, kv head) the cache's 32-entry
+// blocks and then the depth entries' blocks form one list, split evenly into
+// nsplit workgroup parts.  Each part leaves one record per query row in ws:
+// O (unnormalised, kMfmaD floats), reference max (log2 units), weight sum.
 constexpr int kDecodeRecord = kMfmaD + 4;  // floats per record (2 of padding)
 
 struct DecArgs {
   const void *q, *k, *v, *kd, *vd;  // q [B,Hq,d]; k, v [B,Hkv,T,d]; kd, vd [B,Hkv,L,d]
   void *out;                        // [B,Hq,d]
   float *lse;                       // [B,Hq] or null
-  float *ws;                        // [B*Hq, nparts, kDecodeRecord]
+  float *ws;                        // [B*Hq, nsplit, kDecodeRecord]
   int64_t B, Hq, Hkv, T, L;
-  int64_t chunk, nsplit, nparts;
+  int64_t nsplit;
   float scale_log2;  // log2(e) / sqrt(d)
 };
 

@@ -506,3 +506,25 @@ def test_decode_workspace_reuse(m, dev):
         out = m.decode(q, d_in["k"], d_in["v"], kd, vd, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out)
+
+
+def test_decode_graph_replay(m, dev):
+    """The decode step captured in a HIP graph: every replay, with eager work
+    and synchronisations between them, equals the eager result bit for bit."""
+    cfg = shape_cfg(2, 16, 4, 6000, 24, seed=93)
+    d_in, q, kd, vd = decode_case(cfg, dev)
+    sb = m.make_shape(2, 16, 4, 6000, 24, 128, "bf16")
+    ws = torch.empty(m.moda_decode_workspace_bytes(sb), dtype=torch.uint8, device=dev)
+    ref = m.decode(q, d_in["k"], d_in["v"], kd, vd, workspace=ws)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        m.decode(q, d_in["k"], d_in["v"], kd, vd, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        ws.fill_(0x55)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager result"
