@@ -6,9 +6,11 @@ HBM: moda_pack_depth_cache (depth repack) + moda_fwd (fused forward).  The
 causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
 MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
 same packed cache for its HBM rate, and the forward straight from the natural
-depth layout (moda_fwd_natural) for the repack ablation, the decode step
-(moda_decode: the last token over the whole cache) for its HBM rate.  Prints
-one JSON line.
+depth layout (moda_fwd_natural) and from the layer-major one (moda_fwd_layers)
+for the layout ablation, the decode step
+(moda_decode: the last token over the whole cache) and the depth-stream write
+of one entry per token into the packed cache (moda_append_depth) for their
+HBM rates.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
@@ -65,6 +67,11 @@ def depth_bytes(c):
 def pack_bytes(c):
     """Depth K/V read once and written once."""
     return 2 * (2 * c["B"] * c["Hkv"] * c["T"] * c["L"] * c["d"] * es(c))
+
+
+def append_bytes(c, n=1):
+    """Depth-stream write of n entries per token: new K/V read once, written once."""
+    return 2 * (2 * c["B"] * c["Hkv"] * c["T"] * n * c["d"] * es(c))
 
 
 def decode_bytes(c):
@@ -288,6 +295,25 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         moda.fwd_natural(q, k, v, kd, vd, out=nout)
         natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
                                          steps, stream)))
+    layers_ms = None
+    if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
+        # the same entries as per-layer slices [L,B,Hkv,T,d] (moda_fwd_layers)
+        kl = kd.permute(3, 0, 1, 2, 4).contiguous()
+        vl = vd.permute(3, 0, 1, 2, 4).contiguous()
+        lout = torch.empty_like(q)
+        moda.fwd_layers(q, k, v, kl, vl, out=lout)
+        layers_ms = float(np.mean(timed(lambda: moda.fwd_layers(q, k, v, kl, vl, out=lout),
+                                        steps, stream)))
+        del kl, vl, lout
+    append_ms = None
+    if L:
+        # the depth-stream write of one layer: entry L-1 of every token, in place
+        k_new = kd[:, :, :, L - 1].contiguous()
+        v_new = vd[:, :, :, L - 1].contiguous()
+        moda.append_depth(packed, shape, L - 1, k_new, v_new)
+        append_ms = float(np.mean(timed(lambda: moda.append_depth(packed, shape, L - 1, k_new,
+                                                                   v_new), steps, stream)))
+        del k_new, v_new
     depth_ms = None
     if L:
         dout = torch.empty_like(q)
@@ -316,7 +342,8 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
         del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
-               depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms)
+               depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
+               append_ms=append_ms, layers_ms=layers_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -451,6 +478,7 @@ def main():
                               "ratio_fwd_over_causal": r["fwd_ms"] / r["causal_ms"],
                               "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6,
                               "fwd_natural_layout_ms": r["natural_ms"],
+                              "fwd_layer_major_ms": r["layers_ms"],
                               "depth_only_ms": r["depth_ms"],
                               "depth_only_hbm_gbs": (depth_bytes(c) / r["depth_ms"] / 1e6
                                                      if r["depth_ms"] else None),
@@ -495,10 +523,13 @@ def main():
         "depth_only_ms": r["depth_ms"],
         "depth_only_hbm_gbs": depth_bytes(cfg) / r["depth_ms"] / 1e6 if r["depth_ms"] else None,
         "fwd_natural_layout_ms": r["natural_ms"],
+        "fwd_layer_major_ms": r["layers_ms"],
         "bwd_ms": r["bwd_ms"],
         "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
         "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,
         "decode_hbm_gbs": decode_bytes(cfg) / r["decode_ms"] / 1e6 if r["decode_ms"] else None,
+        "append_us": r["append_ms"] * 1e3 if r["append_ms"] else None,
+        "append_hbm_gbs": append_bytes(cfg) / r["append_ms"] / 1e6 if r["append_ms"] else None,
         "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:

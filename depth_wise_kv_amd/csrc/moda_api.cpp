@@ -209,6 +209,30 @@ moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth, cons
   return hip_status(moda::launch_pack_generic(a, s->dtype == MODA_BF16, stream), "pack launch");
 }
 
+moda_status moda_append_depth(const moda_shape *s, int64_t first, int64_t n, const void *k_new,
+                              const void *v_new, void *packed, size_t packed_bytes,
+                              void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_append_depth needs L >= 1");
+  if (n < 1 || first < 0 || first > s->L - n)
+    return fail(MODA_ERR_INVALID_ARG, "entries [first, first + n) must lie in [0, L) with n >= 1");
+  if (!k_new || !v_new || !packed)
+    return fail(MODA_ERR_INVALID_ARG, "k_new, v_new and packed must be non-NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(packed))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t need = cache_bytes(s);
+  if (packed_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(packed_bytes));
+  const int64_t es = s->dtype == MODA_BF16 ? 2 : 4;
+  if ((s->T * n * (use_mfma(s) ? 16 : s->d * es / 16) + 255) / 256 > 0x7FFFFFFFll)
+    return fail(MODA_ERR_UNSUPPORTED, "problem too large for one launch");
+  moda::AppendArgs a{k_new, v_new, packed, s->B, s->Hkv, s->T, s->L, depth_blocks(s), first, n};
+  return hip_status(moda::launch_append(a, use_mfma(s), (int)(s->d * es), (hipStream_t)hip_stream),
+                    "append launch");
+}
+
 moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
                      const void *packed, size_t packed_bytes, void *out, float *lse,
                      void *hip_stream) {
@@ -392,6 +416,35 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
   a.nsplit = decode_splits(s);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
   return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
+}
+
+moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, const void *v,
+                            const void *k_layers, const void *v_layers, void *out, float *lse,
+                            void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (!use_mfma(s))
+    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_layers supports bf16 with d = 128");
+  st = check_qkvo(q, k, v, out, lse);
+  if (st != MODA_OK) return st;
+  if (s->L == 0) {
+    if (k_layers || v_layers)
+      return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
+    return moda_fwd(s, q, k, v, nullptr, 0, out, lse, hip_stream);
+  }
+  if (!k_layers || !v_layers)
+    return fail(MODA_ERR_INVALID_ARG, "k_layers and v_layers must be non-NULL when L > 0");
+  if (!aligned16(k_layers) || !aligned16(v_layers))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (s->T * s->L >= ((int64_t)1 << 23))
+    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_layers supports T * L below 2^23");
+  moda::FwdArgs a = make_fwd_args(s, q, k, v, nullptr, out, lse, true);
+  a.kd_nat = k_layers;
+  a.vd_nat = v_layers;
+  a.depth_layers = true;
+  a.inv_L = 1.0f / (float)s->L;
+  return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), (hipStream_t)hip_stream),
+                    "fwd launch");
 }
 
 const char *moda_status_string(moda_status st) {

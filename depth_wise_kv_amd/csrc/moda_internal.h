@@ -15,7 +15,7 @@ constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part +
 
 struct FwdArgs {
   const void *q, *k, *v, *packed;
-  const void *kd_nat, *vd_nat;  // depth K, V in their natural layout (natural-layout mode)
+  const void *kd_nat, *vd_nat;  // depth K, V read row by row: natural or layer-major layout
   void *out;
   float *lse;
   int64_t B, Hq, Hkv, T, L, d;
@@ -23,6 +23,8 @@ struct FwdArgs {
   float scale_log2;  // log2(e) / sqrt(d)
   bool has_depth;  // the token's depth entries join the softmax
   bool has_seq;    // the causal sequence keys join the softmax
+  bool depth_layers;  // kd_nat, vd_nat are layer-major [L,B,Hkv,T,d] (else [B,Hkv,T,L,d])
+  float inv_L;        // 1 / L (layer-major row lookup)
 };
 
 // Kernel modes: causal attention, MoDA (sequence + depth), depth attention alone.
@@ -30,6 +32,7 @@ constexpr int kModeCausal = 0;
 constexpr int kModeModa = 1;
 constexpr int kModeDepth = 2;
 constexpr int kModeModaNatural = 3;  // MoDA reading depth K, V in their natural layout
+constexpr int kModeModaLayers = 4;   // MoDA reading depth K, V in layer-major layout
 
 struct BwdArgs {
   const void *q, *k, *v, *packed, *kd, *vd, *out, *dout;
@@ -66,6 +69,16 @@ struct PackArgs {
   int64_t nblk;
 };
 
+// Depth-stream write: entries [first, first + n) of every token, from
+// knew, vnew [B,Hkv,T,n,d], into a packed cache of L entries per token.
+struct AppendArgs {
+  const void *knew, *vnew;
+  void *packed;
+  int64_t B, Hkv, T, L;
+  int64_t nblk;  // packed depth blocks per (b, kv head) (MFMA layout)
+  int64_t first, n;
+};
+
 // MFMA path: dtype bf16, d == 128, G divides 32.
 hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s);
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
@@ -75,6 +88,10 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
 // Decode step, bf16, d == 128, G <= 32: partial states, then their merge.
 hipError_t launch_decode(const DecArgs &a, hipStream_t s);
+
+// Depth-stream write into the MFMA block layout (mfma) or the generic one
+// (rows of row_bytes bytes).
+hipError_t launch_append(const AppendArgs &a, bool mfma, int row_bytes, hipStream_t s);
 
 // Generic path: fp32 or bf16, d in {32, 64, 128}, any G.
 hipError_t launch_fwd_generic(const FwdArgs &a, bool bf16, hipStream_t s);

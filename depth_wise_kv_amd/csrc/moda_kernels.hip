@@ -118,7 +118,9 @@ template <int MODE>
 __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   constexpr bool HAS_DEPTH = MODE != kModeCausal;  // depth entries are read
   constexpr bool HAS_SEQ = MODE != kModeDepth;     // sequence keys are read
-  constexpr bool NATURAL = MODE == kModeModaNatural;  // depth K, V in natural layout
+  // depth K, V read row by row (not from the packed cache): natural or layer-major layout
+  constexpr bool NATURAL = MODE == kModeModaNatural || MODE == kModeModaLayers;
+  constexpr bool LAYERS = MODE == kModeModaLayers;
   // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
@@ -179,34 +181,61 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   // operand registers (16 bytes of one row per lane), and its 32 Vd rows go
   // into this wave's 8 KiB of the tile buffers, column-swizzled, to be read
   // transposed as the A operand of O^T += Vd^T P^T.
+  // In the layer-major mode ([L, B, Hkv, T, d]: entry i of every token is one
+  // contiguous [B, Hkv, T, d] tensor, the K or V that layer i wrote) the same
+  // flat (token, entry) blocks are gathered row by row with 64-bit addresses.
   auto depth_natural = [&](int64_t blk_lo, int64_t blk_hi, int64_t my_lo) {
     if constexpr (NATURAL) {
       const int64_t L = p.L, TL = T * L;
-      const __bf16 *knat = (const __bf16 *)p.kd_nat + bh * TL * D;
+      const __bf16 *knat = (const __bf16 *)p.kd_nat + (LAYERS ? 0 : bh * TL * D);
       const __amdgpu_buffer_rsrc_t vd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void *)((const char *)p.vd_nat + bh * TL * (D * 2)), (short)0, (int)(TL * (D * 2)),
           0x00020000);
       char *const slot = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) +
                          (wave & 1) * (TILE_BYTES / 2);
       const TileFrags fr(lane);
+      // row of flat entry e (= token * L + entry, e < T * L < 2^23) in the layer-major
+      // tensor: ((entry * B * Hkv + bh) * T + token)
+      auto layer_row = [&](int64_t e) -> int64_t {
+        const uint32_t eu = (uint32_t)e, Lu = (uint32_t)L;
+        uint32_t t = (uint32_t)((float)eu * p.inv_L);  // floor(e / L), or one off
+        if (t * Lu > eu) --t;
+        else if ((t + 1) * Lu <= eu) ++t;
+        return ((int64_t)(eu - t * Lu) * BH + bh) * T + t;
+      };
       auto load_k = [&](int64_t blk, u32x4 (&kd)[8]) {
         const int64_t e = blk * kDepthBlock + li;
+        const __bf16 *src = knat + (LAYERS ? layer_row(e < TL ? e : 0) : e) * D + 64 * lh;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          kd[ks] = e < TL ? *(const u32x4 *)(knat + e * D + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+          kd[ks] = e < TL ? *(const u32x4 *)(src + 8 * ks) : u32x4{0, 0, 0, 0};
+      };
+      // this wave's Vd rows of block blk into its slot, column-swizzled; a row past
+      // T * L reads zeros (natural) or repeats the last row (layer-major): its weight is 0
+      auto load_v = [&](int64_t blk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const int chunk = 16 * ((lane & 15) ^ (4 * (row & 3)));
+          __attribute__((address_space(3))) void *dst =
+              (__attribute__((address_space(3))) void *)(slot + 4 * i * 256);
+          if constexpr (LAYERS) {
+            const int64_t e = blk * kDepthBlock + row;
+            const char *src =
+                (const char *)p.vd_nat + layer_row(e < TL ? e : TL - 1) * (D * 2) + chunk;
+            __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vd_rsrc, dst, 16,
+                                                     (uint32_t)(row * 256 + chunk),
+                                                     (uint32_t)(blk * kDepthBlock * 256), 0, 0);
+          }
+        }
       };
       u32x4 kd[8];
       load_k(blk_lo, kd);
       for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              vd_rsrc, (__attribute__((address_space(3))) void *)(slot + 4 * i * 256), 16,
-              (uint32_t)(row * 256 + 16 * ((lane & 15) ^ (4 * (row & 3)))),
-              (uint32_t)(blk * kDepthBlock * 256), 0, 0);
-        }
+        load_v(blk);
         floatx16 sd[1];
         floatx16 sd2[2] = {};
 #pragma unroll
@@ -653,7 +682,10 @@ hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t TQ = M / G;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const int64_t grid = ntiles * a.B * a.Hkv;
-  if (a.kd_nat)
+  if (a.kd_nat && a.depth_layers)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers>), dim3((uint32_t)grid), dim3(64 * NWAVE),
+                       0, s, a);
+  else if (a.kd_nat)
     hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural>), dim3((uint32_t)grid), dim3(64 * NWAVE),
                        0, s, a);
   else if (!a.has_seq)

@@ -24,7 +24,8 @@ MODA_F32, MODA_BF16 = 0, 1
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
-           "moda_decode_workspace_bytes", "moda_decode",
+           "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
+           "moda_fwd_layers",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -67,6 +68,10 @@ def _load():
     lib.moda_decode_workspace_bytes.restype = sz
     lib.moda_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moda_decode.restype = ctypes.c_int
+    lib.moda_append_depth.argtypes = [sp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp, sz, vp]
+    lib.moda_append_depth.restype = ctypes.c_int
+    lib.moda_fwd_layers.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moda_fwd_layers.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     lib.moda_last_error.argtypes = []
@@ -150,6 +155,16 @@ def moda_decode(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, ws
                 stream):
     return lib.moda_decode(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr,
                            ws_ptr, ws_bytes, stream)
+
+
+def moda_append_depth(shape, first, n, k_ptr, v_ptr, packed_ptr, packed_bytes, stream):
+    return lib.moda_append_depth(_sref(shape), int(first), int(n), k_ptr, v_ptr, packed_ptr,
+                                 packed_bytes, stream)
+
+
+def moda_fwd_layers(shape, q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr, lse_ptr, stream):
+    return lib.moda_fwd_layers(_sref(shape), q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr,
+                               lse_ptr, stream)
 
 
 def moda_status_string(status: int) -> str:
@@ -277,6 +292,28 @@ def fwd_natural(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, 
     return (out, lse) if with_lse else out
 
 
+def fwd_layers(q, k, v, kl=None, vl=None, L=None, *, with_lse: bool = False, out=None,
+               lse=None):
+    """MoDA forward over a layer-major depth stream kl, vl [Lcap,B,Hkv,T,d]: the
+    first L slices (default: all) are the depth entries."""
+    import torch
+    _check_tensors(q, k, v, kl, vl)
+    B, Hq, T, d = q.shape
+    if kl is None:
+        L = 0
+    elif L is None:
+        L = kl.shape[0]
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(moda_fwd_layers(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kl if L else None),
+                           _ptr(vl if L else None), _ptr(out), _ptr(lse), _stream_ptr(q)),
+           "moda_fwd_layers")
+    return (out, lse) if with_lse else out
+
+
 def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, delta=None):
     """MoDA backward.  ``out`` and ``lse`` come from fwd(..., with_lse=True) on
     the same inputs.  Returns (dq, dk, dv, dkd, dvd); dkd, dvd are None when
@@ -297,6 +334,19 @@ def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, d
                     _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
                     _ptr(dvd), _ptr(delta), _stream_ptr(q)), "moda_bwd")
     return grads
+
+
+def append_depth(packed, shape: ModaShape, first: int, k_new, v_new):
+    """Write entries [first, first + n) of every token into ``packed`` in place;
+    k_new, v_new [B,Hkv,T,n,d] (a [B,Hkv,T,d] pair is taken as n = 1)."""
+    _check_tensors(packed, k_new, v_new)
+    if k_new.dim() == 4:
+        k_new, v_new = k_new.unsqueeze(3), v_new.unsqueeze(3)
+    n = k_new.shape[3]
+    _check(moda_append_depth(shape, first, n, _ptr(k_new), _ptr(v_new), _ptr(packed),
+                             packed.numel() * packed.element_size(), _stream_ptr(k_new)),
+           "moda_append_depth")
+    return packed
 
 
 def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=None,

@@ -84,6 +84,30 @@ moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth,
                                   const void *v_depth, void *packed,
                                   size_t packed_bytes, void *hip_stream);
 
+/* Depth-stream write: store n new depth entries of every token, entries
+ * [first, first + n) of each token's L, into a packed depth cache in place.
+ *
+ * Passage: hyper.ai page on arXiv 2603.15619, section "Depth stream
+ * mechanism": after a layer runs, the keys and values it produced join every
+ * token's depth stream for the layers above; FFN layers add a light KV
+ * projection of their own, so one layer may write two entries.
+ *
+ *   first, n     : the entries written, 0 <= first, n >= 1, first + n <= L
+ *   k_new, v_new : [B, Hkv, T, n, d] (read only): entry first + i of token t
+ *                  of (b, kv head) g is k_new[b, g, t, i, :]
+ *   packed       : a cache of shape `s` (L = the stream's capacity per
+ *                  token), packed_bytes >= moda_depth_cache_bytes(s).  Only
+ *                  the bytes of the written entries change.
+ * A cache that moda_pack_depth_cache wrote, or a zero-filled buffer, is a
+ * valid start: a zero-filled cache after writes of all L entries equals
+ * moda_pack_depth_cache of the same entries, byte for byte.  Entries not yet
+ * written hold whatever the start held (zeros, for a zero-filled one) and
+ * take part in moda_fwd like any other.  Requires L >= 1.  Same validation,
+ * ownership and asynchrony rules as moda_pack_depth_cache. */
+moda_status moda_append_depth(const moda_shape *s, int64_t first, int64_t n,
+                              const void *k_new, const void *v_new, void *packed,
+                              size_t packed_bytes, void *hip_stream);
+
 /* MoDA forward: O (and optionally LSE) from Q, the sequence K/V and the
  * packed depth cache.
  *
@@ -125,6 +149,25 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k,
 moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k,
                              const void *v, const void *k_depth, const void *v_depth,
                              void *out, float *lse, void *hip_stream);
+
+/* MoDA forward reading the depth stream in layer-major order: entry i of
+ * every token is one contiguous tensor [B, Hkv, T, d], the keys (values)
+ * that layer i of the stack produced.  The depth stream then needs no write
+ * step of its own: a layer's K/V projection writes straight into its slice,
+ * and the forward of layer l passes the first l slices with L = l (hyper.ai
+ * page on arXiv 2603.15619, section "Depth stream mechanism": the stream
+ * grows by what each layer writes, and later layers read all of it).
+ * Results are the same as moda_fwd's on the same entries, bit for bit.
+ *
+ *   q, k, v            : as for moda_fwd (read only)
+ *   k_layers, v_layers : depth K, V [L, B, Hkv, T, d] (read only; NULL if L == 0);
+ *                        slices past L may exist and are not read
+ *   out, lse           : as for moda_fwd
+ * Supports bf16 with d = 128 and T * L below 2^23 (MODA_ERR_UNSUPPORTED
+ * otherwise).  Same validation, ownership and asynchrony rules as moda_fwd. */
+moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k,
+                            const void *v, const void *k_layers, const void *v_layers,
+                            void *out, float *lse, void *hip_stream);
 
 /* Depth attention alone: each query row (b, h, t) attends over its own
  * token's L depth entries only, under one softmax scaled by 1/sqrt(d), and

@@ -135,6 +135,35 @@ def test_decode_workspace_and_rejects(m):
     assert "too small" in m.moda_last_error()
 
 
+def test_append_rejects_before_launch(m):
+    s = shape(m, T=100, L=24)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    nb = m.moda_depth_cache_bytes(s)
+    bad = [(s, -1, 1, p, p, p, nb), (s, 0, 0, p, p, p, nb), (s, 23, 2, p, p, p, nb),
+           (s, 24, 1, p, p, p, nb), (s, 0, 1, None, p, p, nb), (s, 0, 1, p, None, p, nb),
+           (s, 0, 1, p, p, None, nb), (s, 0, 1, mis, p, p, nb), (s, 0, 1, p, p, p, nb - 1),
+           (shape(m, L=0), 0, 1, p, p, p, nb), (None, 0, 1, p, p, p, nb)]
+    for args in bad:
+        assert m.moda_append_depth(*args, None) == m.MODA_ERR_INVALID_ARG, args
+    assert m.moda_append_depth(shape(m, d=96), 0, 1, p, p, p, nb, None) == m.MODA_ERR_UNSUPPORTED
+
+
+def test_fwd_layers_rejects_before_launch(m):
+    s = shape(m, T=100, L=24)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    bad = [(s, None, p, p, p, p, p, None), (s, p, p, p, None, p, p, None),
+           (s, p, p, p, p, mis, p, None), (s, p, p, p, p, p, None, None),
+           (shape(m, L=0), p, p, p, p, p, p, None), (None, p, p, p, p, p, p, None)]
+    for args in bad:
+        assert m.moda_fwd_layers(*args, None) == m.MODA_ERR_INVALID_ARG, args
+    assert m.moda_fwd_layers(shape(m, dtype="f32"), p, p, p, p, p, p, None, None) == \
+        m.MODA_ERR_UNSUPPORTED
+    assert m.moda_fwd_layers(shape(m, T=1 << 20, L=8), p, p, p, p, p, p, None, None) == \
+        m.MODA_ERR_UNSUPPORTED
+
+
 def test_binding_refuses_host_tensors(m):
     import torch
     q = torch.zeros(1, 2, 4, 32)

@@ -189,6 +189,45 @@ def test_fwd_natural_matches_packed(m, dev, B, Hq, Hkv, T, L):
     assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
 
 
+def layer_major(t):
+    """[B,Hkv,T,L,d] -> [L,B,Hkv,T,d]: entry i of every token in one slice."""
+    return t.permute(3, 0, 1, 2, 4).contiguous()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
+def test_fwd_layers_matches_packed(m, dev, B, Hq, Hkv, T, L):
+    """moda_fwd_layers (depth stream as per-layer slices [L,B,Hkv,T,d]) gives
+    the packed path's O and LSE bit for bit."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=800 + T + L)
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, L)
+    out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], layer_major(d_in["kd"]),
+                                layer_major(d_in["vd"]), with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
+
+
+def test_fwd_layers_stream_prefix(m, dev):
+    """A layer reads only the first l slices of a longer stream: the forward
+    with L = l over a 40-slice stream equals the oracle on those l entries,
+    and the slices past l are never read (they hold NaN here)."""
+    B, Hq, Hkv, T, Lcap, l = 1, 16, 4, 1500, 40, 13
+    cfg = shape_cfg(B, Hq, Hkv, T, l, seed=901)
+    d_in = device_case(cfg, dev)
+    kl = torch.full((Lcap, B, Hkv, T, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    vl = torch.full_like(kl, float("nan"))
+    kl[:l], vl[:l] = layer_major(d_in["kd"]), layer_major(d_in["vd"])
+    out, lse = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], kl, vl, l, with_lse=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, n_random=16, seed=5)
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
+    e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
+    print(f"[layers] prefix l={l} of {Lcap}: max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
 # ------------------------------------------------------------------ depth attention alone
 
 DEPTH_SHAPES = [  # (B, Hq, Hkv, T, L, d, dtype): MFMA path and generic path, ragged sizes
@@ -528,3 +567,85 @@ def test_decode_graph_replay(m, dev):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i} differs from the eager result"
+
+
+# ------------------------------------------------------------------ depth-stream write
+
+APPEND_SHAPES = [  # (B, Hkv, T, L, group sizes n of the writes, in order of entries)
+    (2, 2, 37, 3, (1, 1, 1)), (1, 4, 100, 24, (2,) * 12), (2, 1, 5, 1, (1,)),
+    (1, 2, 64, 32, (1, 2, 3, 26)), (3, 2, 33, 7, (2, 1, 2, 2)), (1, 1, 1000, 128, (2,) * 64),
+]
+
+
+def write_order(groups, seed):
+    """The groups' entry ranges [first, first + n), in a seeded random order."""
+    firsts = np.cumsum((0,) + tuple(groups))[:-1]
+    order = np.random.default_rng(seed).permutation(len(groups))
+    return [(int(firsts[i]), int(groups[i])) for i in order]
+
+
+@pytest.mark.parametrize("B,Hkv,T,L,groups", APPEND_SHAPES,
+                         ids=[f"B{b}_Hkv{h}_T{t}_L{l}_w{len(g)}" for b, h, t, l, g in APPEND_SHAPES])
+def test_append_builds_the_cache(m, dev, B, Hkv, T, L, groups):
+    """Writing every entry into a zero-filled cache, in any order and group
+    size, gives the packed layout of the natural depth tensor: decoded on the
+    host it is that tensor bit for bit, with zero padding, and it equals
+    moda_pack_depth_cache's bytes."""
+    cfg = shape_cfg(B, 2 * Hkv, Hkv, T, L, seed=500 + T + L)
+    h_in, d_in = host_case(cfg, dev)
+    shape = m.make_shape(B, 2 * Hkv, Hkv, T, L, 128, "bf16")
+    cache = torch.zeros(m.moda_depth_cache_bytes(shape), dtype=torch.uint8, device=dev)
+    for first, n in write_order(groups, seed=T):
+        m.append_depth(cache, shape, first, d_in["kd"][:, :, :, first:first + n].contiguous(),
+                       d_in["vd"][:, :, :, first:first + n].contiguous())
+    ref = m.pack_depth_cache(d_in["kd"], d_in["vd"], shape)
+    torch.cuda.synchronize()
+    K, V = unpack_mfma(cache, B, Hkv, T, L)
+    TL = T * L
+    assert np.array_equal(K[:, :TL], h_in["kd"].reshape(B * Hkv, TL, 128))
+    assert np.array_equal(V[:, :TL], h_in["vd"].reshape(B * Hkv, TL, 128))
+    assert not K[:, TL:].any() and not V[:, TL:].any()
+    assert torch.equal(cache, ref)
+
+
+def test_append_replaces_one_entry(m, dev):
+    """Writing entry i over a packed cache changes exactly entry i of every
+    token: the forward on it equals the forward on a fresh repack of the
+    natural tensor with that entry replaced, bit for bit."""
+    B, Hq, Hkv, T, L, i = 1, 8, 2, 300, 6, 4
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=611)
+    d_in = device_case(cfg, dev)
+    shape = m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")
+    cache = m.pack_depth_cache(d_in["kd"], d_in["vd"], shape)
+    g = torch.Generator(device=dev)
+    g.manual_seed(612)
+    k_new = torch.randn(B, Hkv, T, 128, generator=g, device=dev).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, T, 128, generator=g, device=dev).to(torch.bfloat16)
+    m.append_depth(cache, shape, i, k_new, v_new)
+    kd2, vd2 = d_in["kd"].clone(), d_in["vd"].clone()
+    kd2[:, :, :, i], vd2[:, :, :, i] = k_new, v_new
+    ref = m.pack_depth_cache(kd2, vd2, shape)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, ref)
+    o1 = m.fwd(d_in["q"], d_in["k"], d_in["v"], cache, L)
+    o2 = m.fwd(d_in["q"], d_in["k"], d_in["v"], ref, L)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("d,dt", [(32, "f32"), (64, "bf16"), (128, "f32")])
+def test_append_generic_layout(m, dev, d, dt):
+    """The generic layout (natural Kd then natural Vd): writes of every entry
+    into a zero-filled cache reproduce the natural tensors bit for bit."""
+    B, Hkv, T, L = 2, 2, 19, 5
+    cfg = shape_cfg(B, 2 * Hkv, Hkv, T, L, d=d, dtype=dt, seed=700 + d)
+    h_in, d_in = host_case(cfg, dev)
+    shape = m.make_shape(B, 2 * Hkv, Hkv, T, L, d, dt)
+    cache = torch.zeros(m.moda_depth_cache_bytes(shape), dtype=torch.uint8, device=dev)
+    for first, n in write_order((2, 1, 2), seed=d):
+        m.append_depth(cache, shape, first, d_in["kd"][:, :, :, first:first + n].contiguous(),
+                       d_in["vd"][:, :, :, first:first + n].contiguous())
+    torch.cuda.synchronize()
+    raw = to_np(cache).view(h_in["kd"].dtype)
+    n = h_in["kd"].size
+    assert np.array_equal(raw[:n], h_in["kd"].ravel()) and np.array_equal(raw[n:], h_in["vd"].ravel())
