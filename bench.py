@@ -6,8 +6,10 @@ HBM: moda_pack_depth_cache (depth repack) + moda_fwd (fused forward).  The
 causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
 MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
 same packed cache for its HBM rate, and the forward straight from the natural
-depth layout (moda_fwd_natural) and from the layer-major one (moda_fwd_layers)
-for the layout ablation, the decode step
+depth layout (moda_fwd_natural), from the layer-major one (moda_fwd_layers)
+as a masked scan of the flat depth axis (moda_fwd_masked_scan, T <= 16384
+only), and group-unaware (each query head of a group in its own moda_fwd
+launch, so each reads the depth span itself) for the layout ablation, the decode step
 (moda_decode: the last token over the whole cache) and the depth-stream write
 of one entry per token into the packed cache (moda_append_depth) for their
 HBM rates.  Prints one JSON line.
@@ -295,6 +297,29 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         moda.fwd_natural(q, k, v, kd, vd, out=nout)
         natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
                                          steps, stream)))
+    scan_ms = None
+    if L and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384:
+        # layout ablation: the Flash-compatible masked scan over the flat depth axis
+        sout = torch.empty_like(q)
+        moda.fwd_masked_scan(q, k, v, kd, vd, out=sout)
+        scan_ms = float(np.mean(timed(lambda: moda.fwd_masked_scan(q, k, v, kd, vd, out=sout),
+                                      max(1, steps // 2), stream)))
+        del sout
+    unaware_ms = None
+    G = cfg["Hq"] // cfg["Hkv"]
+    if L and G > 1:
+        # layout ablation, group-unaware: each query head of a group runs on its own (G
+        # launches with one head per KV head), so every head reads the depth span itself
+        q_heads = [q[:, j::G].contiguous() for j in range(G)]
+        o_heads = [torch.empty_like(x) for x in q_heads]
+
+        def unaware():
+            for x, o in zip(q_heads, o_heads):
+                moda.fwd(x, k, v, packed, L, out=o)
+
+        unaware()
+        unaware_ms = float(np.mean(timed(unaware, steps, stream)))
+        del q_heads, o_heads
     layers_ms = None
     if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
         # the same entries as per-layer slices [L,B,Hkv,T,d] (moda_fwd_layers)
@@ -343,7 +368,8 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
-               append_ms=append_ms, layers_ms=layers_ms)
+               append_ms=append_ms, layers_ms=layers_ms, scan_ms=scan_ms,
+               unaware_ms=unaware_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
     del d_in, packed, out
@@ -479,6 +505,8 @@ def main():
                               "fwd_hbm_gbs": fused_bytes(c) / r["fwd_ms"] / 1e6,
                               "fwd_natural_layout_ms": r["natural_ms"],
                               "fwd_layer_major_ms": r["layers_ms"],
+                              "fwd_masked_scan_ms": r["scan_ms"],
+                              "fwd_group_unaware_ms": r["unaware_ms"],
                               "depth_only_ms": r["depth_ms"],
                               "depth_only_hbm_gbs": (depth_bytes(c) / r["depth_ms"] / 1e6
                                                      if r["depth_ms"] else None),
@@ -524,6 +552,8 @@ def main():
         "depth_only_hbm_gbs": depth_bytes(cfg) / r["depth_ms"] / 1e6 if r["depth_ms"] else None,
         "fwd_natural_layout_ms": r["natural_ms"],
         "fwd_layer_major_ms": r["layers_ms"],
+        "fwd_masked_scan_ms": r["scan_ms"],
+        "fwd_group_unaware_ms": r["unaware_ms"],
         "bwd_ms": r["bwd_ms"],
         "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
         "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,

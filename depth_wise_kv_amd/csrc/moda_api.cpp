@@ -447,6 +447,29 @@ moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, c
                     "fwd launch");
 }
 
+moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void *k,
+                                 const void *v, const void *k_depth, const void *v_depth,
+                                 void *out, float *lse, void *hip_stream) {
+  moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  if (!use_mfma(s) || s->L < 1)
+    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_masked_scan supports bf16 with d = 128, L >= 1");
+  st = check_qkvo(q, k, v, out, lse);
+  if (st != MODA_OK) return st;
+  if (!k_depth || !v_depth)
+    return fail(MODA_ERR_INVALID_ARG, "k_depth and v_depth must be non-NULL");
+  if (!aligned16(k_depth) || !aligned16(v_depth))
+    return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (s->T * s->L >= ((int64_t)1 << 23))
+    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_masked_scan supports T * L below 2^23");
+  moda::FwdArgs a = make_fwd_args(s, q, k, v, nullptr, out, lse, true);
+  a.kd_nat = k_depth;
+  a.vd_nat = v_depth;
+  a.depth_scan = true;
+  return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), (hipStream_t)hip_stream),
+                    "fwd launch");
+}
+
 const char *moda_status_string(moda_status st) {
   switch (st) {
     case MODA_OK: return "MODA_OK";

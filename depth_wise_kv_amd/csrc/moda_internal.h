@@ -24,6 +24,7 @@ struct FwdArgs {
   bool has_depth;  // the token's depth entries join the softmax
   bool has_seq;    // the causal sequence keys join the softmax
   bool depth_layers;  // kd_nat, vd_nat are layer-major [L,B,Hkv,T,d] (else [B,Hkv,T,L,d])
+  bool depth_scan;    // natural layout, scanned from entry 0 under the own-token mask
   float inv_L;        // 1 / L (layer-major row lookup)
 };
 
@@ -33,6 +34,7 @@ constexpr int kModeModa = 1;
 constexpr int kModeDepth = 2;
 constexpr int kModeModaNatural = 3;  // MoDA reading depth K, V in their natural layout
 constexpr int kModeModaLayers = 4;   // MoDA reading depth K, V in layer-major layout
+constexpr int kModeModaScan = 5;     // natural layout, every earlier token's entries scanned
 
 struct BwdArgs {
   const void *q, *k, *v, *packed, *kd, *vd, *out, *dout;

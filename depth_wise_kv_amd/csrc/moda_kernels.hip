@@ -119,8 +119,10 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   constexpr bool HAS_DEPTH = MODE != kModeCausal;  // depth entries are read
   constexpr bool HAS_SEQ = MODE != kModeDepth;     // sequence keys are read
   // depth K, V read row by row (not from the packed cache): natural or layer-major layout
-  constexpr bool NATURAL = MODE == kModeModaNatural || MODE == kModeModaLayers;
+  constexpr bool NATURAL =
+      MODE == kModeModaNatural || MODE == kModeModaLayers || MODE == kModeModaScan;
   constexpr bool LAYERS = MODE == kModeModaLayers;
+  constexpr bool SCAN = MODE == kModeModaScan;  // depth scanned from the first token's entries
   // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = M / G;
@@ -273,7 +275,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
       if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
       if (wt_hi > T) wt_hi = T;
       if (L > 0 && wt_lo < wt_hi) {
-        const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
+        // the masked-scan mode (the Flash-compatible layout: depth entries as one causal
+        // key range, each row masked to its own token's entries) starts at entry 0
+        const int64_t blk_lo = SCAN ? 0 : (wt_lo * L) / kDepthBlock;
         const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
         const int64_t my_lo = tok * L;  // this row's entries: [my_lo, my_lo + L)
         if constexpr (NATURAL) {
@@ -684,6 +688,9 @@ hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t grid = ntiles * a.B * a.Hkv;
   if (a.kd_nat && a.depth_layers)
     hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers>), dim3((uint32_t)grid), dim3(64 * NWAVE),
+                       0, s, a);
+  else if (a.kd_nat && a.depth_scan)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaScan>), dim3((uint32_t)grid), dim3(64 * NWAVE),
                        0, s, a);
   else if (a.kd_nat)
     hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural>), dim3((uint32_t)grid), dim3(64 * NWAVE),

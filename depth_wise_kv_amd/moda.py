@@ -25,7 +25,7 @@ MODA_F32, MODA_BF16 = 0, 1
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
            "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
-           "moda_fwd_layers",
+           "moda_fwd_layers", "moda_fwd_masked_scan",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -72,6 +72,8 @@ def _load():
     lib.moda_append_depth.restype = ctypes.c_int
     lib.moda_fwd_layers.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moda_fwd_layers.restype = ctypes.c_int
+    lib.moda_fwd_masked_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moda_fwd_masked_scan.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
     lib.moda_status_string.restype = ctypes.c_char_p
     lib.moda_last_error.argtypes = []
@@ -165,6 +167,11 @@ def moda_append_depth(shape, first, n, k_ptr, v_ptr, packed_ptr, packed_bytes, s
 def moda_fwd_layers(shape, q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr, lse_ptr, stream):
     return lib.moda_fwd_layers(_sref(shape), q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr,
                                lse_ptr, stream)
+
+
+def moda_fwd_masked_scan(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, stream):
+    return lib.moda_fwd_masked_scan(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr,
+                                    lse_ptr, stream)
 
 
 def moda_status_string(status: int) -> str:
@@ -289,6 +296,22 @@ def fwd_natural(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, 
     _check(moda_fwd_natural(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None),
                             _ptr(vd if L else None), _ptr(out), _ptr(lse), _stream_ptr(q)),
            "moda_fwd_natural")
+    return (out, lse) if with_lse else out
+
+
+def fwd_masked_scan(q, k, v, kd, vd, *, with_lse: bool = False, out=None, lse=None):
+    """Layout ablation: moda_fwd_natural's result, with every query tile
+    scanning the flattened depth axis from entry 0 under the own-token mask."""
+    import torch
+    _check_tensors(q, k, v, kd, vd)
+    B, Hq, T, d = q.shape
+    shape = make_shape(B, Hq, k.shape[1], T, kd.shape[3], d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(moda_fwd_masked_scan(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(out),
+                                _ptr(lse), _stream_ptr(q)), "moda_fwd_masked_scan")
     return (out, lse) if with_lse else out
 
 

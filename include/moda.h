@@ -169,6 +169,21 @@ moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k,
                             const void *v, const void *k_layers, const void *v_layers,
                             void *out, float *lse, void *hip_stream);
 
+/* Layout ablation: the MoDA forward with the depth stream handled the way a
+ * FlashAttention-style kernel would see it without a depth-aware layout: the
+ * flattened (token, entry) axis is one causal key range that every query
+ * tile scans from entry 0 up to its last token's entries, with a mask that
+ * keeps each row's own token's L entries only (hyper.ai page on arXiv
+ * 2603.15619, section "Hardware-efficient implementation", names this
+ * Flash-compatible layout and the waste of its masked, out-of-range entries).
+ * The result equals moda_fwd_natural's bit for bit; only the work differs
+ * (about T / (2 * 256 / G) times the depth traffic).  For measurement.
+ *
+ * Arguments, validation and limits as for moda_fwd_natural; requires L >= 1. */
+moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void *k,
+                                 const void *v, const void *k_depth, const void *v_depth,
+                                 void *out, float *lse, void *hip_stream);
+
 /* Depth attention alone: each query row (b, h, t) attends over its own
  * token's L depth entries only, under one softmax scaled by 1/sqrt(d), and
  * gets their weighted values.  No sequence key takes part.

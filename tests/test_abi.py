@@ -164,6 +164,17 @@ def test_fwd_layers_rejects_before_launch(m):
         m.MODA_ERR_UNSUPPORTED
 
 
+def test_fwd_masked_scan_rejects_before_launch(m):
+    s = shape(m, T=100, L=24)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    for args in [(s, None, p, p, p, p, p, None), (s, p, p, p, None, p, p, None),
+                 (s, p, p, p, p, mis, p, None), (None, p, p, p, p, p, p, None)]:
+        assert m.moda_fwd_masked_scan(*args, None) == m.MODA_ERR_INVALID_ARG, args
+    for s2 in (shape(m, L=0), shape(m, dtype="f32"), shape(m, T=1 << 20, L=8)):
+        assert m.moda_fwd_masked_scan(s2, p, p, p, p, p, p, None, None) == m.MODA_ERR_UNSUPPORTED
+
+
 def test_binding_refuses_host_tensors(m):
     import torch
     q = torch.zeros(1, 2, 4, 32)

@@ -208,6 +208,22 @@ def test_fwd_layers_matches_packed(m, dev, B, Hq, Hkv, T, L):
     assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
+def test_fwd_masked_scan_matches_natural(m, dev, B, Hq, Hkv, T, L):
+    """The masked-scan ablation (every earlier token's depth entries scanned,
+    all but the row's own masked out) gives the natural-layout forward's O and
+    LSE bit for bit: the extra blocks carry zero weight."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=900 + T + L)
+    d_in = device_case(cfg, dev)
+    out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                 with_lse=True)
+    out_s, lse_s = m.fwd_masked_scan(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                     with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n, out_s) and torch.equal(lse_n, lse_s)
+
+
 def test_fwd_layers_stream_prefix(m, dev):
     """A layer reads only the first l slices of a longer stream: the forward
     with L = l over a 40-slice stream equals the oracle on those l entries,
