@@ -7,9 +7,10 @@ causal-only mode (moda_causal_fwd) is timed on the same Q/K/V for the
 MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
 same packed cache for its HBM rate, and the forward straight from the natural
 depth layout (moda_fwd_natural), from the layer-major one (moda_fwd_layers)
-as a masked scan of the flat depth axis (moda_fwd_masked_scan, T <= 16384
-only), and group-unaware (each query head of a group in its own moda_fwd
-launch, so each reads the depth span itself) for the layout ablation, the decode step
+and, with --ablation, as a masked scan of the flat depth axis
+(moda_fwd_masked_scan, T <= 16384 only) and group-unaware (each query head of
+a group in its own moda_fwd launch, so each reads the depth span itself) for
+the layout ablation, the decode step
 (moda_decode: the last token over the whole cache) and the depth-stream write
 of one entry per token into the packed cache (moda_append_depth) for their
 HBM rates.  Prints one JSON line.
@@ -89,11 +90,11 @@ def roofline(c, fwd_ms, traffic):
     ai = flops(c) / fused_bytes(c)
     if ai >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         a = flops(c) / fwd_ms / 1e9
-        return {"bound": "mfma", "kernel": "moda_fwd_mfma<true>", "achieved": a,
+        return {"bound": "mfma", "kernel": "moda_fwd_mfma<1>", "achieved": a,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS,
                 "traffic": traffic}
     a = fused_bytes(c) / fwd_ms / 1e6
-    return {"bound": "hbm", "kernel": "moda_fwd_mfma<true>", "achieved": a,
+    return {"bound": "hbm", "kernel": "moda_fwd_mfma<1>", "achieved": a,
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS, "traffic": traffic}
 
 
@@ -247,7 +248,7 @@ def decode_sweep(steps):
         torch.cuda.empty_cache()
 
 
-def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
+def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablation=False):
     import torch
     from depth_wise_kv_amd import moda
     from synth import torch_inputs
@@ -298,7 +299,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
                                          steps, stream)))
     scan_ms = None
-    if L and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384:
+    if ablation and L and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384:
         # layout ablation: the Flash-compatible masked scan over the flat depth axis
         sout = torch.empty_like(q)
         moda.fwd_masked_scan(q, k, v, kd, vd, out=sout)
@@ -307,7 +308,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True):
         del sout
     unaware_ms = None
     G = cfg["Hq"] // cfg["Hkv"]
-    if L and G > 1:
+    if ablation and L and G > 1:
         # layout ablation, group-unaware: each query head of a group runs on its own (G
         # launches with one head per KV head), so every head reads the depth span itself
         q_heads = [q[:, j::G].contiguous() for j in range(G)]
@@ -395,6 +396,9 @@ def profile_only(cfg, which, steps):
     if which == "decode":
         dq, dkd, dvd, dws = decode_inputs(cfg, d_in)
         dout_ = torch.empty_like(dq)
+    if which == "append":
+        k_new = d_in["kd"][:, :, :, L - 1].contiguous()
+        v_new = d_in["vd"][:, :, :, L - 1].contiguous()
     torch.cuda.synchronize()
     for _ in range(steps):
         if which == "fwd":
@@ -405,6 +409,8 @@ def profile_only(cfg, which, steps):
             moda.depth_fwd(d_in["q"], packed, cfg["Hkv"], L, out=out)
         elif which == "decode":
             moda.decode(dq, d_in["k"], d_in["v"], dkd, dvd, out=dout_, workspace=dws)
+        elif which == "append":
+            moda.append_depth(packed, shape, L - 1, k_new, v_new)
         elif which == "bwd":
             moda.bwd(d_in["q"], d_in["k"], d_in["v"], o_b, lse_b, dout, kd, vd, packed)
         else:
@@ -421,11 +427,14 @@ def main():
     ap.add_argument("--config", default="long_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time the group-unaware and masked-scan layout ablations (the "
+                         "group-unaware one launches moda_fwd's kernel at other shapes)")
     ap.add_argument("--decode-sweep", action="store_true",
                     help="time the decode step on the decode shapes (one JSON line each)")
     ap.add_argument("--only", default=None,
                     help="with --sweep: run only points whose name contains this string")
-    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd", "decode"],
+    ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd", "decode", "append"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
                     help="time a bf16 N x N x N torch.matmul (hipBLASLt): the practical "
@@ -495,7 +504,8 @@ def main():
         for c in sweep_points():
             if args.only and args.only not in c["name"]:
                 continue
-            r = bench_config(c, args.steps, args.warmup, False, causal=True, with_bwd=False)
+            r = bench_config(c, args.steps, args.warmup, False, causal=True, with_bwd=False,
+                             ablation=args.ablation)
             print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
                               "pack_ms": r["pack_ms"], "causal_ms": r["causal_ms"],
@@ -516,7 +526,8 @@ def main():
         return
 
     cfg = dict(named[args.config])
-    r = bench_config(cfg, args.steps, args.warmup, not args.no_cpu_baseline)
+    r = bench_config(cfg, args.steps, args.warmup, not args.no_cpu_baseline,
+                     ablation=args.ablation)
     F = flops(cfg)
     step_ms = r["wall_ms"]
     fwd_tflops = F / r["fwd_ms"] / 1e9
