@@ -224,6 +224,36 @@ def test_fwd_masked_scan_matches_natural(m, dev, B, Hq, Hkv, T, L):
     assert torch.equal(out_n, out_s) and torch.equal(lse_n, lse_s)
 
 
+def test_depth_layouts_at_the_index_limit(m, dev):
+    """T * L just below 2^23: the largest depth stream the row-by-row layouts
+    take (a 32-bit flat index; a 2 GiB buffer range for the natural layout's
+    V loads).  Packed, natural and layer-major forwards agree bit for bit, and
+    sampled rows (the last tokens included) match the oracle."""
+    B, Hq, Hkv, T, L = 1, 4, 1, 65535, 128
+    assert T * L < (1 << 23) and T * L * 256 > (1 << 30)
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=1234)
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, L)
+    out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                 with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
+    del out_n, lse_n
+    kl, vl = layer_major(d_in["kd"]), layer_major(d_in["vd"])
+    out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], kl, vl, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
+    del kl, vl, out_l, lse_l
+    rows = sample_rows(cfg, n_random=24, seed=9)
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
+    e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
+    print(f"[limit] T*L={T * L} rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    del d_in, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_fwd_layers_stream_prefix(m, dev):
     """A layer reads only the first l slices of a longer stream: the forward
     with L = l over a 40-slice stream equals the oracle on those l entries,
