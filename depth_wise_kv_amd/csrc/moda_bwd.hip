@@ -531,10 +531,10 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     // the tile needs the causal mask unless its first token is at or past
     // this wave's last key
     const bool masked = tq0 < k0 + 32 * wave + 31;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      // register rr of a 32-row block holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4
-      floatx16 s, dpv;
+    // register rr of a 32-row block sb holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4.
+    // S = Q K^T and dP = dO V^T - D (rows x keys), started from -lse2/c and -D:
+    // two independent MFMA chains, interleaved
+    auto scores = [&](int sb, floatx16 &s, floatx16 &dpv) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row0 = 32 * sb + 8 * g + 4 * lh;
@@ -549,8 +549,6 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         dpv[4 * g + 2] = -d4.z;
         dpv[4 * g + 3] = -d4.w;
       }
-      // S = Q K^T and dP = dO V^T - D (rows x keys): two independent MFMA
-      // chains, interleaved
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(qn, 2 * ks + sb), kb[ks], s, 0, 0,
@@ -558,6 +556,8 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(gn, 2 * ks + sb), vb[ks], dpv, 0,
                                                       0, 0);
       }
+    };
+    auto causal = [&](int sb, floatx16 &s) {
       if (masked) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
@@ -566,29 +566,26 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
           if (tk < key) s[rr] = -INFINITY;
         }
       }
-      // P as fp32 and as bf16 B operands (k-step kk holds registers 8kk .. 8kk+7)
+    };
+    // P and dS = P (dP - D) as bf16 B operands (k-step kk holds registers 8kk .. 8kk+7)
+    auto weights = [&](floatx16 &s, const floatx16 &dpv, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
-      bf16x8 pb[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = cvt_bf16x2(s[8 * kk + 2 * q], s[8 * kk + 2 * q + 1]);
-        pb[kk] = __builtin_bit_cast(bf16x8, w);
-      }
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 w;
+        u32x4 w, wd;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int rr = 8 * kk + 2 * q;
-          w[q] = cvt_bf16x2(s[rr] * dpv[rr], s[rr + 1] * dpv[rr + 1]);
+          w[q] = cvt_bf16x2(s[rr], s[rr + 1]);
+          wd[q] = cvt_bf16x2(s[rr] * dpv[rr], s[rr + 1] * dpv[rr + 1]);
         }
-        dsb[kk] = __builtin_bit_cast(bf16x8, w);
+        pb[kk] = __builtin_bit_cast(bf16x8, w);
+        dsb[kk] = __builtin_bit_cast(bf16x8, wd);
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS  (k-steps 2*sb + kk of the tile)
+    };
+    // dV^T += dO^T P ; dK^T += Q^T dS  (k-steps 2*sb + kk of the tile)
+    auto grads = [&](int sb, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -598,7 +595,22 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
           dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(qtr, 4 * nb + 2 * sb + kk),
                                                            dsb[kk], dk[nb], 0, 0, 0);
         }
-    }
+    };
+    // Two-stage pipeline over the tile's two 32-row blocks: block 1's score
+    // MFMAs are issued before block 0's exponentials, and block 0's gradient
+    // MFMAs before block 1's, so the matrix core runs while the wave's own
+    // VALU works (one wave per SIMD: no other wave fills those gaps).
+    floatx16 s0, d0, s1, d1;
+    scores(0, s0, d0);
+    causal(0, s0);
+    scores(1, s1, d1);
+    bf16x8 pb0[2], ds0[2];
+    weights(s0, d0, pb0, ds0);
+    causal(1, s1);
+    grads(0, pb0, ds0);
+    bf16x8 pb1[2], ds1[2];
+    weights(s1, d1, pb1, ds1);
+    grads(1, pb1, ds1);
     wait_vmem();
     if (more && wave == 0) {
       lse_s[P ^ 1][lane] = l2n;
