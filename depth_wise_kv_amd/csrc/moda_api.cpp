@@ -168,6 +168,48 @@ size_t decode_ws_bytes(const moda_shape *s) {
   return (size_t)(s->B * s->Hq * decode_splits(s) * moda::kDecodeRecord * 4);
 }
 
+moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
+                        const void *k_cache, const void *v_cache, const void *k_depth,
+                        const void *v_depth, void *out, float *lse, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
+  moda_status st = check_decode_shape(s);
+  if (st != MODA_OK) return st;
+  st = check_qkvo(q, k_cache, v_cache, out, lse);
+  if (st != MODA_OK) return st;
+  if (s->L > 0) {
+    if (!k_depth || !v_depth)
+      return fail(MODA_ERR_INVALID_ARG, "k_depth and v_depth must be non-NULL when L > 0");
+    if (!aligned16(k_depth) || !aligned16(v_depth))
+      return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  } else if (k_depth || v_depth) {
+    return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
+  }
+  if (!workspace || !aligned16(workspace))
+    return fail(MODA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
+  const size_t need = decode_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+  moda::DecArgs a{};
+  a.q = q;
+  a.lens = lens;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.kd = k_depth;
+  a.vd = v_depth;
+  a.out = out;
+  a.lse = lse;
+  a.ws = (float *)workspace;
+  a.B = s->B;
+  a.Hq = s->Hq;
+  a.Hkv = s->Hkv;
+  a.T = s->T;
+  a.L = s->L;
+  a.nsplit = decode_splits(s);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
+  return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,41 +423,19 @@ size_t moda_decode_workspace_bytes(const moda_shape *s) {
 moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
                         const void *v_cache, const void *k_depth, const void *v_depth, void *out,
                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
-  moda_status st = check_decode_shape(s);
-  if (st != MODA_OK) return st;
-  st = check_qkvo(q, k_cache, v_cache, out, lse);
-  if (st != MODA_OK) return st;
-  if (s->L > 0) {
-    if (!k_depth || !v_depth)
-      return fail(MODA_ERR_INVALID_ARG, "k_depth and v_depth must be non-NULL when L > 0");
-    if (!aligned16(k_depth) || !aligned16(v_depth))
-      return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  } else if (k_depth || v_depth) {
-    return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
-  }
-  if (!workspace || !aligned16(workspace))
-    return fail(MODA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
-  const size_t need = decode_ws_bytes(s);
-  if (workspace_bytes < need)
-    return fail(MODA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need) +
-                                          " bytes, got " + std::to_string(workspace_bytes));
-  moda::DecArgs a{};
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.kd = k_depth;
-  a.vd = v_depth;
-  a.out = out;
-  a.lse = lse;
-  a.ws = (float *)workspace;
-  a.B = s->B;
-  a.Hq = s->Hq;
-  a.Hkv = s->Hkv;
-  a.T = s->T;
-  a.L = s->L;
-  a.nsplit = decode_splits(s);
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
-  return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
+  return decode_impl(s, nullptr, q, k_cache, v_cache, k_depth, v_depth, out, lse, workspace,
+                     workspace_bytes, hip_stream);
+}
+
+moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, const void *q,
+                               const void *k_cache, const void *v_cache, const void *k_depth,
+                               const void *v_depth, void *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  if (!cache_lens) return fail(MODA_ERR_INVALID_ARG, "cache_lens must be non-NULL");
+  if (((uintptr_t)cache_lens & 3u) != 0)
+    return fail(MODA_ERR_INVALID_ARG, "cache_lens must be 4-byte aligned");
+  return decode_impl(s, cache_lens, q, k_cache, v_cache, k_depth, v_depth, out, lse, workspace,
+                     workspace_bytes, hip_stream);
 }
 
 moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, const void *v,

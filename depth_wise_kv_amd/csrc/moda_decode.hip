@@ -63,12 +63,21 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
   // nbc blocks, then the depth entries' blocks.  This part takes blocks
   // [j_lo, j_hi) of it; wave w takes every DEC_WAVES-th of those from j_lo + w.
   const int64_t nbc = (p.T + 31) / 32;
+  // entries of this sequence's cache (the first n_c of its T slots)
+  int64_t n_c = p.T;
+  if (p.lens) {
+    const int64_t len = p.lens[b];
+    n_c = len < 0 ? 0 : (len > p.T ? p.T : len);
+  }
+  const int64_t jc_end = (n_c + 31) / 32;  // cache blocks [jc_end, nbc) hold no entry
   const int64_t nb = nbc + (p.L + 31) / 32;
   const int64_t j_lo = part * nb / p.nsplit, j_hi = (part + 1) * nb / p.nsplit;
   const __bf16 *kc = (const __bf16 *)p.k + bh * p.T * DEC_D;
   const __bf16 *kdp = (const __bf16 *)p.kd + bh * p.L * DEC_D;
+  // (the V descriptor ends at the sequence's last entry: the rest of its slots
+  // may hold anything, and a masked row must still read as finite zeros)
   const __amdgpu_buffer_rsrc_t vc_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const char *)p.v + bh * p.T * (DEC_D * 2)), (short)0, (int)(p.T * (DEC_D * 2)),
+      (void *)((const char *)p.v + bh * p.T * (DEC_D * 2)), (short)0, (int)(n_c * (DEC_D * 2)),
       0x00020000);
   const __amdgpu_buffer_rsrc_t vd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.vd + bh * p.L * (DEC_D * 2)), (short)0, (int)(p.L * (DEC_D * 2)),
@@ -87,18 +96,25 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
   auto load_k = [&](int64_t j, u32x4 (&kd)[8]) {
     const bool dep = j >= nbc;
     const int64_t e = (dep ? j - nbc : j) * 32 + li;
-    const int64_t n = dep ? p.L : p.T;
+    const int64_t n = dep ? p.L : n_c;
     const __bf16 *src = (dep ? kdp : kc) + e * DEC_D + 64 * lh;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       kd[ks] = e < n ? *(const u32x4 *)(src + 8 * ks) : u32x4{0, 0, 0, 0};
   };
+  // this wave's blocks: every DEC_WAVES-th from j_lo + wave, stepping over the
+  // empty cache blocks, so that every block visited has an entry in lane 0
+  auto skip_empty = [&](int64_t j) -> int64_t {
+    return (j >= jc_end && j < nbc) ? j + (nbc - j + DEC_WAVES - 1) / DEC_WAVES * DEC_WAVES : j;
+  };
   u32x4 kd[8];
-  if (j_lo + wave < j_hi) load_k(j_lo + wave, kd);
-  for (int64_t j = j_lo + wave; j < j_hi; j += DEC_WAVES) {
+  const int64_t j_first = skip_empty(j_lo + wave);
+  if (j_first < j_hi) load_k(j_first, kd);
+  for (int64_t j = j_first, jn; j < j_hi; j = jn) {
+    jn = skip_empty(j + DEC_WAVES);
     const bool dep = j >= nbc;
     const int64_t e0 = (dep ? j - nbc : j) * 32;
-    const int64_t n = dep ? p.L : p.T;
+    const int64_t n = dep ? p.L : n_c;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
     // V rows e0 .. e0+31 into the slot, column-swizzled (rows past the source read as zeros)
 #pragma unroll
@@ -119,8 +135,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
                                                             qb[ks], sd2[ks & 1], 0, 0, 0);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
-    const bool more = j + DEC_WAVES < j_hi;
-    if (more) load_k(j + DEC_WAVES, kd);
+    const bool more = jn < j_hi;
+    if (more) load_k(jn, kd);
     // register rr holds entry e0 + 8*(rr/4) + 4*lh + rr%4: entries past the source drop out
     const int64_t lim64 = n - e0 - 4 * lh;
     const int lim = (int)(lim64 > 64 ? 64 : lim64);
@@ -249,9 +265,11 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p)
     O0 += o_s[w][2 * lane] * c;
     O1 += o_s[w][2 * lane + 1] * c;
   }
-  const float inv = 1.0f / L;
+  // a row with no entry (empty cache and L = 0) gets O = 0 and LSE = -inf
+  const float inv = M == -INFINITY ? 0.f : 1.0f / L;
   *(uint32_t *)((__bf16 *)p.out + row * DEC_D + 2 * lane) = cvt_bf16x2(O0 * inv, O1 * inv);
-  if (p.lse && lane == 0) p.lse[row] = (M + __log2f(L)) * 0.69314718055994531f;
+  if (p.lse && lane == 0)
+    p.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 hipError_t launch_decode(const DecArgs &a, hipStream_t s) {

@@ -56,6 +56,7 @@ constexpr int kDecodeRecord = kMfmaD + 4;  // floats per record (2 of padding)
 
 struct DecArgs {
   const void *q, *k, *v, *kd, *vd;  // q [B,Hq,d]; k, v [B,Hkv,T,d]; kd, vd [B,Hkv,L,d]
+  const int32_t *lens;              // [B] cache entries per sequence (<= T), or null: all T
   void *out;                        // [B,Hq,d]
   float *lse;                       // [B,Hq] or null
   float *ws;                        // [B*Hq, nsplit, kDecodeRecord]

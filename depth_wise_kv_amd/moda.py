@@ -25,7 +25,7 @@ MODA_F32, MODA_BF16 = 0, 1
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
            "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
-           "moda_fwd_layers", "moda_fwd_masked_scan",
+           "moda_fwd_layers", "moda_fwd_masked_scan", "moda_decode_varlen",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -72,6 +72,8 @@ def _load():
     lib.moda_append_depth.restype = ctypes.c_int
     lib.moda_fwd_layers.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moda_fwd_layers.restype = ctypes.c_int
+    lib.moda_decode_varlen.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moda_decode_varlen.restype = ctypes.c_int
     lib.moda_fwd_masked_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moda_fwd_masked_scan.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +169,12 @@ def moda_append_depth(shape, first, n, k_ptr, v_ptr, packed_ptr, packed_bytes, s
 def moda_fwd_layers(shape, q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr, lse_ptr, stream):
     return lib.moda_fwd_layers(_sref(shape), q_ptr, k_ptr, v_ptr, kl_ptr, vl_ptr, out_ptr,
                                lse_ptr, stream)
+
+
+def moda_decode_varlen(shape, lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr,
+                       ws_ptr, ws_bytes, stream):
+    return lib.moda_decode_varlen(_sref(shape), lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr,
+                                  out_ptr, lse_ptr, ws_ptr, ws_bytes, stream)
 
 
 def moda_fwd_masked_scan(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, stream):
@@ -373,13 +381,14 @@ def append_depth(packed, shape: ModaShape, first: int, k_new, v_new):
 
 
 def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=None,
-           workspace=None):
+           workspace=None, cache_lens=None):
     """Decode step: q [B,Hq,d] of the new token over the cache k, v [B,Hkv,T,d]
     (the new token's own K, V last) and its depth entries kd, vd [B,Hkv,L,d].
-    ``workspace`` may pass a uint8 device tensor of at least
-    moda_decode_workspace_bytes bytes."""
+    ``cache_lens`` (int32 device tensor [B]) gives each sequence's cache length
+    (T is then the capacity).  ``workspace`` may pass a uint8 device tensor of
+    at least moda_decode_workspace_bytes bytes."""
     import torch
-    _check_tensors(q, k, v, kd, vd)
+    _check_tensors(q, k, v, kd, vd, cache_lens)
     B, Hq, d = q.shape
     T = k.shape[2]
     L = 0 if kd is None else kd.shape[2]
@@ -391,10 +400,15 @@ def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=N
         out = torch.empty_like(q)
     if with_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    _check(moda_decode(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None),
-                       _ptr(vd if L else None), _ptr(out), _ptr(lse), _ptr(workspace),
-                       workspace.numel() * workspace.element_size(), _stream_ptr(q)),
-           "moda_decode")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None), _ptr(vd if L else None),
+            _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_ptr(q))
+    if cache_lens is None:
+        _check(moda_decode(shape, *args), "moda_decode")
+    else:
+        if cache_lens.dtype != torch.int32 or cache_lens.numel() != B:
+            raise ValueError("cache_lens must be an int32 tensor of B elements")
+        _check(moda_decode_varlen(shape, _ptr(cache_lens), *args), "moda_decode_varlen")
     return (out, lse) if with_lse else out
 
 

@@ -262,6 +262,23 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
                         void *out, float *lse, void *workspace, size_t workspace_bytes,
                         void *hip_stream);
 
+/* Decode step over caches of different lengths: as moda_decode, but sequence
+ * b's cache holds cache_lens[b] entries, the first slots of its T (T is the
+ * capacity; the new token's K/V is entry cache_lens[b] - 1).  Row (b, h) is
+ * the forward's row t = cache_lens[b] - 1 of a sequence of that length.
+ *
+ *   cache_lens : device int32 [B] (read only), 4-byte aligned; values are
+ *                clamped to [0, T].  A sequence of length 0 attends over its
+ *                depth entries alone; with L == 0 as well its rows get O = 0
+ *                and LSE = -inf.
+ * The slots past a sequence's length are never read, whatever they hold.
+ * Other arguments, the workspace size (moda_decode_workspace_bytes(s)) and
+ * the limits are those of moda_decode. */
+moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, const void *q,
+                               const void *k_cache, const void *v_cache, const void *k_depth,
+                               const void *v_depth, void *out, float *lse, void *workspace,
+                               size_t workspace_bytes, void *hip_stream);
+
 /* Static text of a status code (never NULL). */
 const char *moda_status_string(moda_status st);
 

@@ -133,6 +133,14 @@ def test_decode_workspace_and_rejects(m):
     assert m.moda_decode(s, p, p, p, p, p, p, None, mis, ws, None) == m.MODA_ERR_INVALID_ARG
     assert m.moda_decode(s, p, p, p, p, p, p, None, p, ws - 1, None) == m.MODA_ERR_INVALID_ARG
     assert "too small" in m.moda_last_error()
+    # the ragged form also needs its length array (device int32, 4-byte aligned)
+    odd = ctypes.c_void_p(4096 + 2)
+    assert m.moda_decode_varlen(s, None, p, p, p, p, p, p, None, p, ws, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode_varlen(s, odd, p, p, p, p, p, p, None, p, ws, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode_varlen(s, p, p, p, p, p, p, p, None, p, ws - 1, None) == \
+        m.MODA_ERR_INVALID_ARG
 
 
 def test_append_rejects_before_launch(m):

@@ -593,6 +593,67 @@ def test_decode_workspace_reuse(m, dev):
         assert torch.equal(out, ref_out)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", [(5, 16, 4, 3000, 5), (3, 8, 8, 700, 0), (2, 32, 1, 5000, 24),
+                                          (4, 6, 2, 129, 128)],
+                         ids=["B5_G4_L5", "B3_G1_L0", "B2_G32_L24", "B4_G3_L128"])
+def test_decode_varlen_parity(m, dev, B, Hq, Hkv, T, L):
+    """Sequences of different cache lengths in one call (T is the capacity):
+    row (b, h) against the oracle's row t = len_b - 1.  The slots past each
+    length hold NaN and are never read."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=1500 + T + L)
+    d_in = device_case(cfg, dev)
+    rng = np.random.default_rng(T + L)
+    lens = np.concatenate([[1, T], rng.integers(1, T + 1, size=B)])[:B].astype(np.int32)
+    k, v = d_in["k"].clone(), d_in["v"].clone()
+    for b in range(B):
+        k[b, :, int(lens[b]):] = float("nan")
+        v[b, :, int(lens[b]):] = float("nan")
+    bi = torch.arange(B, device=dev)
+    tl = torch.from_numpy(lens.astype(np.int64) - 1).to(dev)
+    q = d_in["q"][bi, :, tl].contiguous()                               # [B, Hq, d]
+    kd = d_in["kd"][bi, :, tl].contiguous() if L else None              # [B, Hkv, L, d]
+    vd = d_in["vd"][bi, :, tl].contiguous() if L else None
+    out, lse = m.decode(q, k, v, kd, vd, with_lse=True,
+                        cache_lens=torch.from_numpy(lens).to(dev))
+    torch.cuda.synchronize()
+    rows = np.array([(b, h, int(lens[b]) - 1) for b in range(B) for h in range(Hq)], np.int64)
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    e_o = max_err(out_to_f64(out).reshape(B * Hq, -1), ref)
+    e_l = max_err(lse.cpu().numpy().reshape(-1), rlse)
+    print(f"[decode varlen] lens={lens.tolist()} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+
+
+def test_decode_varlen_edges(m, dev):
+    """Length 0 leaves the depth entries alone (depth attention over the L
+    entries); length 0 with L = 0 gives O = 0 and LSE = -inf; lengths all equal
+    to T give moda_decode's result bit for bit."""
+    B, Hq, Hkv, T, L = 3, 8, 2, 400, 6
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=1601)
+    d_in, q, kd, vd = decode_case(cfg, dev)
+    full = torch.full((B,), T, dtype=torch.int32, device=dev)
+    o_full = m.decode(q, d_in["k"], d_in["v"], kd, vd, cache_lens=full)
+    o_ref = m.decode(q, d_in["k"], d_in["v"], kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o_full, o_ref)
+    zero = torch.tensor([0, T, 0], dtype=torch.int32, device=dev)
+    out, lse = m.decode(q, d_in["k"], d_in["v"], kd, vd, with_lse=True, cache_lens=zero)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    q1 = to_np(q[0::2].unsqueeze(2))                                  # rows of b = 0, 2 as T = 1
+    kd1 = to_np(kd[0::2].unsqueeze(2))
+    vd1 = to_np(vd[0::2].unsqueeze(2))
+    ref, rlse = oracle.depth_forward(q1, kd1, vd1)
+    e_o = max_err(out_to_f64(out[0::2]), ref[:, :, 0])
+    e_l = max_err(lse[0::2].cpu().numpy(), rlse[:, :, 0])
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    assert torch.equal(out[1], o_ref[1])
+    out0, lse0 = m.decode(q, d_in["k"], d_in["v"], with_lse=True, cache_lens=zero)
+    torch.cuda.synchronize()
+    assert not out0[0::2].float().abs().any() and torch.isneginf(lse0[0::2]).all()
+    assert torch.isfinite(lse0[1]).all()
+
+
 def test_decode_graph_replay(m, dev):
     """The decode step captured in a HIP graph: every replay, with eager work
     and synchronisations between them, equals the eager result bit for bit."""
