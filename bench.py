@@ -340,6 +340,15 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         append_ms = float(np.mean(timed(lambda: moda.append_depth(packed, shape, L - 1, k_new,
                                                                    v_new), steps, stream)))
         del k_new, v_new
+    append2_ms = None
+    if L >= 2:
+        # a layer that writes two entries (attention K/V and the FFN's KV projection)
+        k_new = kd[:, :, :, L - 2:].contiguous()
+        v_new = vd[:, :, :, L - 2:].contiguous()
+        moda.append_depth(packed, shape, L - 2, k_new, v_new)
+        append2_ms = float(np.mean(timed(lambda: moda.append_depth(packed, shape, L - 2, k_new,
+                                                                    v_new), steps, stream)))
+        del k_new, v_new
     depth_ms = None
     if L:
         dout = torch.empty_like(q)
@@ -369,7 +378,8 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         del o_b, lse_b, dout, grads, delta
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
-               append_ms=append_ms, layers_ms=layers_ms, scan_ms=scan_ms,
+               append_ms=append_ms, append2_ms=append2_ms, layers_ms=layers_ms,
+               scan_ms=scan_ms,
                unaware_ms=unaware_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
@@ -571,6 +581,9 @@ def main():
         "decode_hbm_gbs": decode_bytes(cfg) / r["decode_ms"] / 1e6 if r["decode_ms"] else None,
         "append_us": r["append_ms"] * 1e3 if r["append_ms"] else None,
         "append_hbm_gbs": append_bytes(cfg) / r["append_ms"] / 1e6 if r["append_ms"] else None,
+        "append2_us": r["append2_ms"] * 1e3 if r["append2_ms"] else None,
+        "append2_hbm_gbs": (append_bytes(cfg, 2) / r["append2_ms"] / 1e6
+                            if r["append2_ms"] else None),
         "roofline": roofline(cfg, r["fwd_ms"], traffic),
     }
     if "cpu_baseline" in r:
