@@ -8,9 +8,10 @@ MoDA / causal-only time ratio, depth attention alone (moda_depth_fwd) on the
 same packed cache for its HBM rate, and the forward straight from the natural
 depth layout (moda_fwd_natural), from the layer-major one (moda_fwd_layers)
 and, with --ablation, as a masked scan of the flat depth axis
-(moda_fwd_masked_scan, T <= 16384 only) and group-unaware (each query head of
-a group in its own moda_fwd launch, so each reads the depth span itself) for
-the layout ablation, the decode step
+(moda_fwd_masked_scan, T <= 16384 only), group-unaware (each query head of a
+group in its own moda_fwd launch, so each reads the depth span itself) and as
+a naive per-token loop (T decode calls, T <= 16384 only) for the layout
+ablation, the decode step
 (moda_decode: the last token over the whole cache) and the depth-stream write
 of one entry per token into the packed cache (moda_append_depth) for their
 HBM rates.  Prints one JSON line.
@@ -321,6 +322,29 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         unaware()
         unaware_ms = float(np.mean(timed(unaware, steps, stream)))
         del q_heads, o_heads
+    pertoken_ms = None
+    if (ablation and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384
+            and cfg["Hq"] // cfg["Hkv"] <= 32):
+        # layout ablation, naive per-token loop: token t alone (one decode call over the
+        # cache's first t+1 keys and its own depth entries), T launches from the host
+        T = cfg["T"]
+        q_t = q.permute(2, 0, 1, 3).contiguous()
+        kd_t = kd.permute(2, 0, 1, 3, 4).contiguous() if L else None
+        vd_t = vd.permute(2, 0, 1, 3, 4).contiguous() if L else None
+        lens = (torch.arange(1, T + 1, dtype=torch.int32, device=dev)[:, None]
+                .expand(T, cfg["B"]).contiguous())
+        o_t = torch.empty_like(q_t)
+        ws = torch.empty(max(16, moda.moda_decode_workspace_bytes(shape)), dtype=torch.uint8,
+                         device=dev)
+
+        def pertoken():
+            for t in range(T):
+                moda.decode(q_t[t], k, v, kd_t[t] if L else None, vd_t[t] if L else None,
+                            out=o_t[t], workspace=ws, cache_lens=lens[t])
+
+        pertoken()
+        pertoken_ms = float(np.mean(timed(pertoken, 2, stream)))
+        del q_t, kd_t, vd_t, lens, o_t, ws
     layers_ms = None
     if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
         # the same entries as per-layer slices [L,B,Hkv,T,d] (moda_fwd_layers)
@@ -379,7 +403,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
                append_ms=append_ms, append2_ms=append2_ms, layers_ms=layers_ms,
-               scan_ms=scan_ms,
+               scan_ms=scan_ms, pertoken_ms=pertoken_ms,
                unaware_ms=unaware_ms)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, d_in)
@@ -575,6 +599,7 @@ def main():
         "fwd_layer_major_ms": r["layers_ms"],
         "fwd_masked_scan_ms": r["scan_ms"],
         "fwd_group_unaware_ms": r["unaware_ms"],
+        "fwd_per_token_loop_ms": r["pertoken_ms"],
         "bwd_ms": r["bwd_ms"],
         "bwd_tflops": 2.5 * F / r["bwd_ms"] / 1e9 if r["bwd_ms"] else None,
         "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,

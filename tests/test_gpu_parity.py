@@ -654,6 +654,26 @@ def test_decode_varlen_edges(m, dev):
     assert torch.isfinite(lse0[1]).all()
 
 
+def test_decode_per_token_loop_is_the_forward(m, dev):
+    """Decoding every token in turn (cache length t+1 within the full cache,
+    the token's own depth entries) gives the forward's rows: each against the
+    full fp64 oracle."""
+    B, Hq, Hkv, T, L = 2, 8, 2, 70, 5
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=1701)
+    h_in, d_in = host_case(cfg, dev)
+    out = torch.empty_like(d_in["q"])
+    for t in range(T):
+        lens = torch.full((B,), t + 1, dtype=torch.int32, device=dev)
+        out[:, :, t] = m.decode(d_in["q"][:, :, t].contiguous(), d_in["k"], d_in["v"],
+                                d_in["kd"][:, :, t].contiguous(), d_in["vd"][:, :, t].contiguous(),
+                                cache_lens=lens)
+    torch.cuda.synchronize()
+    ref, _ = oracle.moda_forward(h_in["q"], h_in["k"], h_in["v"], h_in["kd"], h_in["vd"])
+    e_o = max_err(out_to_f64(out), ref)
+    print(f"[decode loop] T={T} max|dO|={e_o:.3e}", flush=True)
+    assert e_o <= BF16_TOL
+
+
 def test_decode_graph_replay(m, dev):
     """The decode step captured in a HIP graph: every replay, with eager work
     and synchronisations between them, equals the eager result bit for bit."""
