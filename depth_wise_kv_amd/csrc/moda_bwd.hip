@@ -718,16 +718,20 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
     // S_d = Q Kd^T (rows x entries)
     floatx16 sd;
     row_init(lse_s, neg_inv_c, sd);
-    {
-      u32x4 kd[8];
+    // the block's Kd rows (packed K half) and Vd rows (natural): all sixteen
+    // loads in flight before the first MFMA waits
+    u32x4 kd[8], vr[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
+    for (int ks = 0; ks < 8; ++ks)
+      kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]),
-                                                     sd, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      vr[ks] = e < TL ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]), sd,
+                                                   0, 0, 0);
     // keep (row, entry) iff the entry is one of the row's token's entries
     const int64_t etok = e / L - wt_lo;  // the entry's token, relative
 #pragma unroll
@@ -740,17 +744,10 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
     // dP_d = dO Vd^T - D
     floatx16 dpd;
     row_init(del_s, -1.0f, dpd);
-    {
-      const bool e_ok = e < TL;
-      u32x4 vr[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        vr[ks] = e_ok ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
-                                                      dpd, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
+                                                    dpd, 0, 0, 0);
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
