@@ -19,6 +19,7 @@ HBM rates.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
     python bench.py --decode-sweep     # one JSON line per decode shape
+    python bench.py --stack --config layer_1p5b   # a stack of layers growing the depth stream
 
 FLOP convention (algorithmic, per query head): 4 * d * (T(T+1)/2 + T*L), the
 diagonal counted, exponentials not counted.  The backward (moda_bwd, timed
@@ -226,6 +227,64 @@ def time_decode(cfg, d_in, steps, stream, reps=20, given=None):
 DECODE_SWEEP = [(1, 16, 4, 65536, 32), (4, 32, 8, 8192, 128), (2, 16, 4, 4096, 24),
                 (1, 16, 4, 4096, 24), (32, 16, 4, 8192, 24), (64, 16, 4, 4096, 24),
                 (8, 32, 8, 32768, 64), (16, 16, 16, 16384, 32)]
+
+
+def stack_run(cfg, steps):
+    """A stack of L+1 layers at one layer's shape, each attending over the depth
+    entries its predecessors wrote (layer l: L = l), three ways:
+      layer-major stream: layer l writes its K/V as slice l of [L+1, B, Hkv, T, d]
+        (zero-copy) and moda_fwd_layers reads the first l slices;
+      packed, repacked per layer: the first l entries repacked, then moda_fwd;
+      natural, per layer: moda_fwd_natural over a contiguous [B, Hkv, T, l, d];
+      natural with room: layer l writes entry l of [B, Hkv, T, L+1, d] in place
+        and moda_fwd_strided reads the first l entries of every token.
+    Inputs are reused across layers (timing only).  Prints one JSON line."""
+    import torch
+    from depth_wise_kv_amd import moda
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    B, Hq, Hkv, T, NL, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["L"] + 1, cfg["d"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000)
+    r = lambda *sh: torch.randn(*sh, generator=g, device=dev).to(torch.bfloat16)
+    q, k, v = r(B, Hq, T, d), r(B, Hkv, T, d), r(B, Hkv, T, d)
+    kl, vl = r(NL, B, Hkv, T, d), r(NL, B, Hkv, T, d)
+    out = torch.empty_like(q)
+    nat = {l: (kl[:l].permute(1, 2, 3, 0, 4).contiguous(), vl[:l].permute(1, 2, 3, 0, 4).contiguous())
+           for l in range(1, NL)}
+    packed = {l: torch.empty(moda.moda_depth_cache_bytes(moda.make_shape(B, Hq, Hkv, T, l, d, "bf16")),
+                             dtype=torch.uint8, device=dev) for l in range(1, NL)}
+
+    def layer_major():
+        for l in range(NL):
+            moda.fwd_layers(q, k, v, kl if l else None, vl if l else None, l, out=out)
+
+    def packed_per_layer():
+        for l in range(NL):
+            if l:
+                shape = moda.make_shape(B, Hq, Hkv, T, l, d, "bf16")
+                moda.pack_depth_cache(nat[l][0], nat[l][1], shape, out=packed[l])
+                moda.fwd(q, k, v, packed[l], l, out=out)
+            else:
+                moda.fwd(q, k, v, None, 0, out=out)
+
+    kc, vc = kl.permute(1, 2, 3, 0, 4).contiguous(), vl.permute(1, 2, 3, 0, 4).contiguous()
+
+    def natural_room():
+        for l in range(NL):
+            moda.fwd_capacity(q, k, v, kc if l else None, vc if l else None, l, out=out)
+
+    def natural_per_layer():
+        for l in range(NL):
+            moda.fwd_natural(q, k, v, nat[l][0] if l else None, nat[l][1] if l else None, out=out)
+
+    res = {"stack": f"{NL} layers at B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}, layer l reads l depth entries"}
+    for name, fn in (("layer_major_ms", layer_major), ("packed_repack_per_layer_ms", packed_per_layer),
+                     ("natural_per_layer_ms", natural_per_layer),
+                     ("natural_with_room_ms", natural_room)):
+        fn()
+        res[name] = float(np.mean(timed(fn, steps, stream)))
+    print(json.dumps(res), flush=True)
 
 
 def decode_sweep(steps):
@@ -464,6 +523,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="also time the group-unaware and masked-scan layout ablations (the "
                          "group-unaware one launches moda_fwd's kernel at other shapes)")
+    ap.add_argument("--stack", action="store_true",
+                    help="time a stack of L+1 layers at the config's shape (layer l reads l depth "
+                         "entries): layer-major stream vs per-layer repack vs natural layout")
     ap.add_argument("--decode-sweep", action="store_true",
                     help="time the decode step on the decode shapes (one JSON line each)")
     ap.add_argument("--only", default=None,
@@ -533,6 +595,9 @@ def main():
 
     if args.decode_sweep:
         decode_sweep(args.steps)
+        return
+    if args.stack:
+        stack_run(dict(named[args.config]), args.steps)
         return
     if args.sweep:
         for c in sweep_points():

@@ -438,33 +438,55 @@ moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, c
                      workspace_bytes, hip_stream);
 }
 
-moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, const void *v,
-                            const void *k_layers, const void *v_layers, void *out, float *lse,
-                            void *hip_stream) {
+moda_status moda_fwd_strided(const moda_shape *s, const void *q, const void *k, const void *v,
+                             const void *k_depth, const void *v_depth, int64_t stride_bh,
+                             int64_t stride_t, int64_t stride_i, void *out, float *lse,
+                             void *hip_stream) {
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (!use_mfma(s))
-    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_layers supports bf16 with d = 128");
+    return fail(MODA_ERR_UNSUPPORTED, "the strided depth forward supports bf16 with d = 128");
   st = check_qkvo(q, k, v, out, lse);
   if (st != MODA_OK) return st;
   if (s->L == 0) {
-    if (k_layers || v_layers)
+    if (k_depth || v_depth)
       return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
     return moda_fwd(s, q, k, v, nullptr, 0, out, lse, hip_stream);
   }
-  if (!k_layers || !v_layers)
-    return fail(MODA_ERR_INVALID_ARG, "k_layers and v_layers must be non-NULL when L > 0");
-  if (!aligned16(k_layers) || !aligned16(v_layers))
+  if (!k_depth || !v_depth)
+    return fail(MODA_ERR_INVALID_ARG, "depth inputs must be non-NULL when L > 0");
+  if (!aligned16(k_depth) || !aligned16(v_depth))
     return fail(MODA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (stride_bh < 0 || stride_t < 0 || stride_i < 0)
+    return fail(MODA_ERR_INVALID_ARG, "depth strides must be >= 0");
   if (s->T * s->L >= ((int64_t)1 << 23))
-    return fail(MODA_ERR_UNSUPPORTED, "moda_fwd_layers supports T * L below 2^23");
+    return fail(MODA_ERR_UNSUPPORTED, "the strided depth forward supports T * L below 2^23");
+  // the largest row index must stay addressable
+  const int64_t last = checked_prod({s->B * s->Hkv - 1, stride_bh});
+  const int64_t last_t = checked_prod({s->T - 1, stride_t});
+  const int64_t last_i = checked_prod({s->L - 1, stride_i});
+  if (last < 0 || last_t < 0 || last_i < 0 || last + last_t + last_i >= ((int64_t)1 << 54))
+    return fail(MODA_ERR_INVALID_ARG, "depth strides address rows beyond 2^54");
   moda::FwdArgs a = make_fwd_args(s, q, k, v, nullptr, out, lse, true);
-  a.kd_nat = k_layers;
-  a.vd_nat = v_layers;
+  a.kd_nat = k_depth;
+  a.vd_nat = v_depth;
   a.depth_layers = true;
   a.inv_L = 1.0f / (float)s->L;
+  a.ds_bh = stride_bh;
+  a.ds_t = stride_t;
+  a.ds_i = stride_i;
   return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), (hipStream_t)hip_stream),
                     "fwd launch");
+}
+
+moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, const void *v,
+                            const void *k_layers, const void *v_layers, void *out, float *lse,
+                            void *hip_stream) {
+  const moda_status st = moda_check_shape(s);
+  if (st != MODA_OK) return st;
+  // [L, B, Hkv, T, d]: row (b, g, t, i) at (i * B * Hkv + b * Hkv + g) * T + t
+  return moda_fwd_strided(s, q, k, v, k_layers, v_layers, s->T, 1, s->B * s->Hkv * s->T, out,
+                          lse, hip_stream);
 }
 
 moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void *k,

@@ -23,9 +23,10 @@ struct FwdArgs {
   float scale_log2;  // log2(e) / sqrt(d)
   bool has_depth;  // the token's depth entries join the softmax
   bool has_seq;    // the causal sequence keys join the softmax
-  bool depth_layers;  // kd_nat, vd_nat are layer-major [L,B,Hkv,T,d] (else [B,Hkv,T,L,d])
+  bool depth_layers;  // kd_nat, vd_nat rows are strided (ds_*) (else [B,Hkv,T,L,d])
   bool depth_scan;    // natural layout, scanned from entry 0 under the own-token mask
-  float inv_L;        // 1 / L (layer-major row lookup)
+  float inv_L;        // 1 / L (strided row lookup)
+  int64_t ds_bh, ds_t, ds_i;  // strided depth rows: (b, g, t, i) at bh*ds_bh + t*ds_t + i*ds_i
 };
 
 // Kernel modes: causal attention, MoDA (sequence + depth), depth attention alone.
@@ -33,7 +34,7 @@ constexpr int kModeCausal = 0;
 constexpr int kModeModa = 1;
 constexpr int kModeDepth = 2;
 constexpr int kModeModaNatural = 3;  // MoDA reading depth K, V in their natural layout
-constexpr int kModeModaLayers = 4;   // MoDA reading depth K, V in layer-major layout
+constexpr int kModeModaLayers = 4;   // MoDA reading depth K, V rows at given strides
 constexpr int kModeModaScan = 5;     // natural layout, every earlier token's entries scanned
 
 struct BwdArgs {

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   // depth K, V read row by row (not from the packed cache): natural or layer-major layout
   constexpr bool NATURAL =
       MODE == kModeModaNatural || MODE == kModeModaLayers || MODE == kModeModaScan;
-  constexpr bool LAYERS = MODE == kModeModaLayers;
+  constexpr bool LAYERS = MODE == kModeModaLayers;  // strided depth rows
   constexpr bool SCAN = MODE == kModeModaScan;  // depth scanned from the first token's entries
   // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
@@ -183,9 +183,11 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
   // operand registers (16 bytes of one row per lane), and its 32 Vd rows go
   // into this wave's 8 KiB of the tile buffers, column-swizzled, to be read
   // transposed as the A operand of O^T += Vd^T P^T.
-  // In the layer-major mode ([L, B, Hkv, T, d]: entry i of every token is one
-  // contiguous [B, Hkv, T, d] tensor, the K or V that layer i wrote) the same
-  // flat (token, entry) blocks are gathered row by row with 64-bit addresses.
+  // In the strided mode (row (b, g, token, entry) of the depth K and V at
+  // (b*Hkv + g) * s_bh + token * s_t + entry * s_i: e.g. layer-major
+  // [Lcap, B, Hkv, T, d], where entry i of every token is the K or V layer i
+  // wrote, or [B, Hkv, T, Lcap, d] with room for more entries) the same flat
+  // (token, entry) blocks are gathered row by row with 64-bit addresses.
   auto depth_natural = [&](int64_t blk_lo, int64_t blk_hi, int64_t my_lo) {
     if constexpr (NATURAL) {
       const int64_t L = p.L, TL = T * L;
@@ -196,14 +198,14 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
       char *const slot = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) +
                          (wave & 1) * (TILE_BYTES / 2);
       const TileFrags fr(lane);
-      // row of flat entry e (= token * L + entry, e < T * L < 2^23) in the layer-major
-      // tensor: ((entry * B * Hkv + bh) * T + token)
+      // row of flat entry e (= token * L + entry, e < T * L < 2^23) in the strided
+      // depth tensors: bh * s_bh + token * s_t + entry * s_i (rows of d elements)
       auto layer_row = [&](int64_t e) -> int64_t {
         const uint32_t eu = (uint32_t)e, Lu = (uint32_t)L;
         uint32_t t = (uint32_t)((float)eu * p.inv_L);  // floor(e / L), or one off
         if (t * Lu > eu) --t;
         else if ((t + 1) * Lu <= eu) ++t;
-        return ((int64_t)(eu - t * Lu) * BH + bh) * T + t;
+        return bh * p.ds_bh + (int64_t)t * p.ds_t + (int64_t)(eu - t * Lu) * p.ds_i;
       };
       auto load_k = [&](int64_t blk, u32x4 (&kd)[8]) {
         const int64_t e = blk * kDepthBlock + li;

@@ -26,6 +26,7 @@ EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache"
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
            "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
            "moda_fwd_layers", "moda_fwd_masked_scan", "moda_decode_varlen",
+           "moda_fwd_strided",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -74,6 +75,9 @@ def _load():
     lib.moda_fwd_layers.restype = ctypes.c_int
     lib.moda_decode_varlen.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moda_decode_varlen.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.moda_fwd_strided.argtypes = [sp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.moda_fwd_strided.restype = ctypes.c_int
     lib.moda_fwd_masked_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moda_fwd_masked_scan.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
@@ -175,6 +179,12 @@ def moda_decode_varlen(shape, lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out
                        ws_ptr, ws_bytes, stream):
     return lib.moda_decode_varlen(_sref(shape), lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr,
                                   out_ptr, lse_ptr, ws_ptr, ws_bytes, stream)
+
+
+def moda_fwd_strided(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, s_bh, s_t, s_i, out_ptr, lse_ptr,
+                     stream):
+    return lib.moda_fwd_strided(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, int(s_bh),
+                                int(s_t), int(s_i), out_ptr, lse_ptr, stream)
 
 
 def moda_fwd_masked_scan(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr, stream):
@@ -320,6 +330,27 @@ def fwd_masked_scan(q, k, v, kd, vd, *, with_lse: bool = False, out=None, lse=No
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     _check(moda_fwd_masked_scan(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(out),
                                 _ptr(lse), _stream_ptr(q)), "moda_fwd_masked_scan")
+    return (out, lse) if with_lse else out
+
+
+def fwd_capacity(q, k, v, kd=None, vd=None, L=None, *, with_lse: bool = False, out=None,
+                 lse=None):
+    """MoDA forward over a natural-layout depth stream with room for more
+    entries: kd, vd [B,Hkv,T,Lcap,d], of which the first L (default: all) are
+    the depth entries (moda_fwd_strided with strides (T*Lcap, Lcap, 1))."""
+    import torch
+    _check_tensors(q, k, v, kd, vd)
+    B, Hq, T, d = q.shape
+    Lcap = 0 if kd is None else kd.shape[3]
+    L = Lcap if L is None else L
+    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(moda_fwd_strided(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd if L else None),
+                            _ptr(vd if L else None), T * Lcap, Lcap, 1, _ptr(out), _ptr(lse),
+                            _stream_ptr(q)), "moda_fwd_strided")
     return (out, lse) if with_lse else out
 
 

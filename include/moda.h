@@ -184,6 +184,26 @@ moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void 
                                  const void *v, const void *k_depth, const void *v_depth,
                                  void *out, float *lse, void *hip_stream);
 
+/* MoDA forward reading depth K and V rows at caller-given strides: row
+ * (b, g, t, i) of each (the i-th depth entry of token t of KV head g of
+ * sequence b) starts at element ((b * Hkv + g) * stride_bh + t * stride_t +
+ * i * stride_i) * d of k_depth (v_depth), for i < L.  moda_fwd_layers is the
+ * case (T, 1, B * Hkv * T); a natural-layout stream with room for Lcap
+ * entries per token, [B, Hkv, T, Lcap, d] of which the first L are written,
+ * is (T * Lcap, Lcap, 1).  Either lets each layer write its entry in place
+ * and the next layer read the stream as it stands (hyper.ai page on arXiv
+ * 2603.15619, section "Depth stream mechanism").  Results are the same as
+ * moda_fwd's on the same entries, bit for bit; rows outside the L entries are
+ * never read.
+ *
+ * Strides are in rows of d elements, each >= 0; every addressed row must lie
+ * inside the caller's buffers.  Supports bf16 with d = 128 and T * L below
+ * 2^23.  Same validation, ownership and asynchrony rules as moda_fwd. */
+moda_status moda_fwd_strided(const moda_shape *s, const void *q, const void *k,
+                             const void *v, const void *k_depth, const void *v_depth,
+                             int64_t stride_bh, int64_t stride_t, int64_t stride_i,
+                             void *out, float *lse, void *hip_stream);
+
 /* Depth attention alone: each query row (b, h, t) attends over its own
  * token's L depth entries only, under one softmax scaled by 1/sqrt(d), and
  * gets their weighted values.  No sequence key takes part.

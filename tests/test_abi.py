@@ -183,6 +183,23 @@ def test_fwd_masked_scan_rejects_before_launch(m):
         assert m.moda_fwd_masked_scan(s2, p, p, p, p, p, p, None, None) == m.MODA_ERR_UNSUPPORTED
 
 
+def test_fwd_strided_rejects_before_launch(m):
+    s = shape(m, T=100, L=24)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    ok = (100 * 24, 24, 1)
+    assert m.moda_fwd_strided(s, p, p, p, None, p, *ok, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd_strided(s, p, p, p, mis, p, *ok, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd_strided(s, p, p, p, p, p, -1, 24, 1, p, None, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd_strided(s, p, p, p, p, p, 1 << 60, 24, 1, p, None, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd_strided(shape(m, T=100, L=0), p, p, p, p, p, *ok, p, None, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_fwd_strided(shape(m, dtype="f32"), p, p, p, p, p, *ok, p, None, None) == \
+        m.MODA_ERR_UNSUPPORTED
+    assert m.moda_fwd_strided(None, p, p, p, p, p, *ok, p, None, None) == m.MODA_ERR_INVALID_ARG
+
+
 def test_binding_refuses_host_tensors(m):
     import torch
     q = torch.zeros(1, 2, 4, 32)

@@ -254,6 +254,24 @@ def test_depth_layouts_at_the_index_limit(m, dev):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
+def test_fwd_capacity_matches_packed(m, dev, B, Hq, Hkv, T, L):
+    """A natural-layout stream with room for 7 more entries per token (the
+    spare slots hold NaN): the strided forward over its first L entries gives
+    the packed path's O and LSE bit for bit."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, seed=820 + T + L)
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, L)
+    cap = L + 7
+    kc = torch.full((B, Hkv, T, cap, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    kc[:, :, :, :L], vc[:, :, :, :L] = d_in["kd"], d_in["vd"]
+    out_c, lse_c = m.fwd_capacity(d_in["q"], d_in["k"], d_in["v"], kc, vc, L, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_c) and torch.equal(lse, lse_c)
+
+
 def test_fwd_layers_stream_prefix(m, dev):
     """A layer reads only the first l slices of a longer stream: the forward
     with L = l over a 40-slice stream equals the oracle on those l entries,
