@@ -85,6 +85,14 @@ def decode_bytes(c):
     return es(c) * (2 * B * Hkv * T * d + 2 * B * Hkv * L * d + 2 * B * Hq * d)
 
 
+def fwd_kernel_name(c):
+    """Name of the fused kernel instance moda_fwd launches for workload c."""
+    from depth_wise_kv_amd import moda
+    v = moda.moda_fwd_variant(moda.make_shape(c["B"], c["Hq"], c["Hkv"], c["T"], c["L"], c["d"],
+                                              c["dtype"]))
+    return "moda_fwd_mfma<1, 4>" if v.endswith("_w4") else "moda_fwd_mfma<1, 8>"
+
+
 def roofline(c, fwd_ms, traffic):
     """Roofline of the fused kernel: matrix-core-bound when its arithmetic
     intensity (algorithmic flops per algorithmic HBM byte) is above the ridge
@@ -92,11 +100,11 @@ def roofline(c, fwd_ms, traffic):
     ai = flops(c) / fused_bytes(c)
     if ai >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         a = flops(c) / fwd_ms / 1e9
-        return {"bound": "mfma", "kernel": "moda_fwd_mfma<1>", "achieved": a,
+        return {"bound": "mfma", "kernel": fwd_kernel_name(c), "achieved": a,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS,
                 "traffic": traffic}
     a = fused_bytes(c) / fwd_ms / 1e6
-    return {"bound": "hbm", "kernel": "moda_fwd_mfma<1>", "achieved": a,
+    return {"bound": "hbm", "kernel": fwd_kernel_name(c), "achieved": a,
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS, "traffic": traffic}
 
 

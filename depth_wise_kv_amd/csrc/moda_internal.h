@@ -9,7 +9,7 @@ namespace moda {
 
 // Geometry of the MFMA path (bf16, head dim 128).
 constexpr int kMfmaD = 128;         // head dimension
-constexpr int kMfmaRows = 256;      // query rows (token x head pairs) per workgroup
+constexpr int kMfmaRows = 256;      // query rows (token x head pairs) per 8-wave workgroup
 constexpr int kDepthBlock = 32;     // depth entries per packed block
 constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part + V part
 
@@ -84,7 +84,8 @@ struct AppendArgs {
 };
 
 // MFMA path: dtype bf16, d == 128, G divides 32.
-hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s);
+// waves = 8 (256 rows per workgroup) or 4 (128 rows); G <= 32 * waves.
+hipError_t launch_fwd_mfma(const FwdArgs &a, int G, int waves, hipStream_t s);
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
 
 // Backward, bf16, d == 128, G <= 64: delta, dQ, then dK/dV.

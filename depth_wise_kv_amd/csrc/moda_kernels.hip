@@ -50,7 +50,6 @@ __device__ __forceinline__ float wave_swap32(float x) {
 // sum are in-lane work plus one exchange with lane l ^ 32.
 // ---------------------------------------------------------------------------
 constexpr int D = kMfmaD;             // 128
-constexpr int M = kMfmaRows;          // 256 query rows per workgroup
 constexpr int NKEY = 64;              // keys per sequence tile
 constexpr int BLK_HALF = kDepthBlock * D * 2;  // bytes of the K (or V) half of a packed block
 
@@ -87,7 +86,8 @@ __device__ unsigned long long moda_trace_buf[16];
 // Fused forward, MFMA path.
 //
 // A workgroup has 8 waves and owns 256 query rows (32 per wave): two waves on
-// every SIMD, and each K/V tile brought into LDS serves 256 rows.  K and V tiles of 64
+// every SIMD, and each K/V tile brought into LDS serves 256 rows.  (Small
+// grids use 4-wave workgroups of 128 rows instead, two per CU.)  K and V tiles of 64
 // keys go straight from global memory into LDS (buffer_load_dwordx4 ... lds), no
 // registers in between, into XOR-swizzled 16 KiB buffers:
 //   K: 16-byte chunk c of key row r sits in slot c ^ (r % 16)    (ds_read_b128
@@ -103,10 +103,6 @@ __device__ unsigned long long moda_trace_buf[16];
 // compiler can see that the loads in flight never alias the buffers read.
 // ---------------------------------------------------------------------------
 constexpr int TILE_BYTES = NKEY * D * 2;  // 16 KiB: one K or V tile
-constexpr int NWAVE = M / 32;             // waves per workgroup, 32 query rows each
-constexpr int DMA_ROWS = NKEY / NWAVE;    // tile rows each wave loads
-constexpr int DMA_INSTR = DMA_ROWS / 4;   // 1 KiB (4-row) load instructions per wave per tile
-static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divide the MFMAs");
 
 // Order of the 16 PV MFMAs: fragment f = 4*nb + kk feeds accumulator nb with
 // key step kk.  Going round-robin over the four accumulators keeps
@@ -114,8 +110,16 @@ static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divi
 __device__ __forceinline__ constexpr int pv_order(int i) { return 4 * (i & 3) + (i >> 2); }
 
 
-template <int MODE>
-__global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
+// NW waves of 32 query rows each: 8 (one workgroup per CU, two waves per
+// SIMD) or 4 (two workgroups per CU, for grids too small to fill the chip
+// several times over with 256-row tiles).
+template <int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
+  constexpr int NWAVE = NW;                  // waves per workgroup
+  constexpr int MR = 32 * NW;                // query rows per workgroup
+  constexpr int DMA_ROWS = NKEY / NWAVE;     // tile rows each wave loads
+  constexpr int DMA_INSTR = DMA_ROWS / 4;    // 1 KiB (4-row) load instructions per wave per tile
+  static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divide the MFMAs");
   constexpr bool HAS_DEPTH = MODE != kModeCausal;  // depth entries are read
   constexpr bool HAS_SEQ = MODE != kModeDepth;     // sequence keys are read
   // depth K, V read row by row (not from the packed cache): natural or layer-major layout
@@ -123,9 +127,9 @@ __global__ __launch_bounds__(64 * NWAVE, 1) void moda_fwd_mfma(FwdArgs p) {
       MODE == kModeModaNatural || MODE == kModeModaLayers || MODE == kModeModaScan;
   constexpr bool LAYERS = MODE == kModeModaLayers;  // strided depth rows
   constexpr bool SCAN = MODE == kModeModaScan;  // depth scanned from the first token's entries
-  // A tile holds TQ = floor(256 / G) tokens x G heads; rows past TQ * G idle.
+  // A tile holds TQ = floor(MR / G) tokens x G heads; rows past TQ * G idle.
   const int G = (int)(p.Hq / p.Hkv);
-  const int TQ = M / G;
+  const int TQ = MR / G;
   __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
@@ -683,30 +687,31 @@ __global__ __launch_bounds__(256) void moda_copy_generic(const u32x4 *kd, const 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_fwd_mfma(const FwdArgs &a, int G, hipStream_t s) {
-  if (G < 1 || G > M) return hipErrorInvalidValue;
-  const int64_t TQ = M / G;
+template <int NW>
+static hipError_t launch_fwd_nw(const FwdArgs &a, int G, hipStream_t s) {
+  if (G < 1 || G > 32 * NW) return hipErrorInvalidValue;
+  const int64_t TQ = 32 * NW / G;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
-  const int64_t grid = ntiles * a.B * a.Hkv;
+  const dim3 grid((uint32_t)(ntiles * a.B * a.Hkv)), block(64 * NW);
   if (a.kd_nat && a.depth_layers)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers>), dim3((uint32_t)grid), dim3(64 * NWAVE),
-                       0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers, NW>), grid, block, 0, s, a);
   else if (a.kd_nat && a.depth_scan)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaScan>), dim3((uint32_t)grid), dim3(64 * NWAVE),
-                       0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaScan, NW>), grid, block, 0, s, a);
   else if (a.kd_nat)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural>), dim3((uint32_t)grid), dim3(64 * NWAVE),
-                       0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural, NW>), grid, block, 0, s, a);
   else if (!a.has_seq)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
-                       a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth, NW>), grid, block, 0, s, a);
   else if (a.has_depth)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
-                       a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa, NW>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s,
-                       a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal, NW>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const FwdArgs &a, int G, int waves, hipStream_t s) {
+  if (waves == 4) return launch_fwd_nw<4>(a, G, s);
+  if (waves == 8) return launch_fwd_nw<8>(a, G, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s) {

@@ -61,7 +61,10 @@ def test_depth_cache_bytes(m):
     assert m.moda_depth_cache_bytes(shape(m, dtype="f32", d=32, T=64, L=4, Hkv=1, Hq=2)) == \
         2 * 64 * 4 * 32 * 4
     assert m.moda_depth_cache_bytes(shape(m, Hq=15)) == 0
-    assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128"
+    # 4-wave workgroups when the 256-row grid fills the chip at most twice over
+    assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128_w4"
+    assert m.moda_fwd_variant(shape(m, T=65536)) == "mfma_bf16_d128_w8"
+    assert m.moda_fwd_variant(shape(m, Hq=256, Hkv=1)) == "mfma_bf16_d128_w8"   # G > 128
     assert m.moda_fwd_variant(shape(m, dtype="f32")) == "generic"
     assert m.moda_fwd_variant(shape(m, d=64)) == "generic"
 

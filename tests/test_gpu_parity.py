@@ -79,7 +79,8 @@ MFMA_SHAPES = [
                          ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in MFMA_SHAPES])
 def test_mfma_path_small(m, dev, B, Hq, Hkv, T, L):
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=11 + T + 7 * L)
-    assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) == "mfma_bf16_d128"
+    assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")).startswith(
+        "mfma_bf16_d128")
     check_full(m, cfg, dev)
 
 
