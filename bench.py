@@ -130,15 +130,18 @@ def load_traffic(name):
 
 
 def timed(fn, steps, stream):
+    """Mean duration (ms) of fn over `steps` back-to-back calls, from HIP events
+    recorded on the stream the kernels run on (one pair around all calls, so
+    the host's launch cost hides behind the queued work)."""
     import torch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / steps]
 
 
 def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
