@@ -404,16 +404,22 @@ constexpr int KV_DMA = KV_ROWS / 4;        // 4-row load instructions per copy
 __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQr = QROWS / G;  // tokens per query tile (G <= 64)
-  __shared__ __attribute__((aligned(1024))) char qn0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char qn1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char qt0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char qt1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char gn0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char gn1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char gt0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char gt1[BTILE];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];
-  __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];
+  // Distinct objects, so that the compiler sees that loads in flight into one
+  // parity's buffers never alias the other parity's being read.  c* hold the
+  // column-swizzled copies (read transposed), r* the row-swizzled ones; the
+  // compiler lays out equally aligned LDS objects in name order, which puts
+  // the c* tiles in the low 64 KiB, where every transposed read reaches its
+  // address through the 16-bit offset field.
+  __shared__ __attribute__((aligned(1024))) char cq0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char cq1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char cg0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char cg1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char rq0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char rq1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char rg0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char rg1[BTILE];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];  // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];  // -D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,7 +449,6 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     for (int rr = 0; rr < 16; ++rr) dk[nb][rr] = dv[nb][rr] = 0.f;
 
   const float c = p.scale_log2;
-  const float neg_inv_c = -1.0f / c;
   // query tiles: tokens from k0 (the first that sees a key of this workgroup)
   const int64_t n_qt = (T - k0 + TQr - 1) / TQr;
 
@@ -478,38 +483,42 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
       dma16(g_rsrc, gtr + lrow, off_c[i], soff);
     }
   };
-  // lse2 and D of tile row `lane` (wave 0 only): rows outside the problem get
-  // lse2 = +inf (weight 0) and D = 0
-  auto row_stats = [&](int64_t qt, float &l2, float &dl) {
+  // lse and D of tile row `lane`, loaded by every wave without a branch (rows
+  // outside the problem read row 0 and are replaced when stored).  Nothing
+  // uses them until the tile's loads have landed: a use right after the load
+  // would make the wave wait for the tile loads issued before it.
+  struct RowStats {
+    float l, dl;
+    bool ok;
+  };
+  auto row_stats = [&](int64_t qt) {
     const int row = lane;
     const int64_t tk = k0 + qt * TQr + row / G;
-    if (row < TQr * G && tk < T) {
-      const int64_t qr = (grp + row % G) * T + tk;
-      l2 = p.lse[qr] * LOG2E;
-      dl = p.delta[qr];
-    } else {
-      l2 = INFINITY;
-      dl = 0.f;
-    }
+    const bool ok = row < TQr * G && tk < T;
+    const int64_t qr = ok ? (grp + row % G) * T + tk : 0;
+    return RowStats{p.lse[qr], p.delta[qr], ok};
+  };
+  // -lse * log2(e) and -D; rows outside the problem get weight 0
+  auto store_stats = [&](int buf, const RowStats &r) {
+    lse_s[buf][lane] = r.ok ? -LOG2E * r.l : -INFINITY;
+    del_s[buf][lane] = r.ok ? -r.dl : 0.f;
   };
 
   for (int o = tid * 16; o < BTILE; o += 64 * KV_WAVES * 16) {
-    *(u32x4 *)(qn0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(qn1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(qt0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(qt1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(gn0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(gn1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(gt0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(gt1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(rq0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(rq1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(cq0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(cq1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(rg0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(rg1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(cg0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(cg1 + o) = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  dma_tile(0, qn0, qt0, gn0, gt0);
-  if (wave == 0) {
-    float l2, dl;
-    row_stats(0, l2, dl);
-    lse_s[0][lane] = l2;
-    del_s[0][lane] = dl;
+  dma_tile(0, rq0, cq0, rg0, cg0);
+  {
+    const RowStats r0 = row_stats(0);
+    if (wave == 0) store_stats(0, r0);
   }
   wait_vmem();
   __syncthreads();
@@ -517,38 +526,22 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   // query tile qt in buffers of parity P; loads of tile qt+1 are issued first
   auto body = [&](int64_t qt, auto parity) {
     constexpr int P = decltype(parity)::value;
-    const char *const qn = P ? qn1 : qn0;
-    const char *const qtr = P ? qt1 : qt0;
-    const char *const gn = P ? gn1 : gn0;
-    const char *const gtr = P ? gt1 : gt0;
-    float l2n = 0.f, dln = 0.f;
+    const char *const qn = P ? rq1 : rq0;
+    const char *const qtr = P ? cq1 : cq0;
+    const char *const gn = P ? rg1 : rg0;
+    const char *const gtr = P ? cg1 : cg0;
     const bool more = qt + 1 < n_qt;
-    if (more) {
-      dma_tile(qt + 1, P ? qn0 : qn1, P ? qt0 : qt1, P ? gn0 : gn1, P ? gt0 : gt1);
-      if (wave == 0) row_stats(qt + 1, l2n, dln);
-    }
+    if (more) dma_tile(qt + 1, P ? rq0 : rq1, P ? cq0 : cq1, P ? rg0 : rg1, P ? cg0 : cg1);
+    const RowStats rn = row_stats(qt + 1);
     const int64_t tq0 = k0 + qt * TQr;  // first token of the tile
     // the tile needs the causal mask unless its first token is at or past
     // this wave's last key
     const bool masked = tq0 < k0 + 32 * wave + 31;
     // register rr of a 32-row block sb holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4.
-    // S = Q K^T and dP = dO V^T - D (rows x keys), started from -lse2/c and -D:
-    // two independent MFMA chains, interleaved
+    // S = Q K^T and dP = dO V^T (rows x keys): two independent MFMA chains, interleaved
     auto scores = [&](int sb, floatx16 &s, floatx16 &dpv) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row0 = 32 * sb + 8 * g + 4 * lh;
-        const float4 l4 = *(const float4 *)&lse_s[P][row0];
-        const float4 d4 = *(const float4 *)&del_s[P][row0];
-        s[4 * g + 0] = l4.x * neg_inv_c;
-        s[4 * g + 1] = l4.y * neg_inv_c;
-        s[4 * g + 2] = l4.z * neg_inv_c;
-        s[4 * g + 3] = l4.w * neg_inv_c;
-        dpv[4 * g + 0] = -d4.x;
-        dpv[4 * g + 1] = -d4.y;
-        dpv[4 * g + 2] = -d4.z;
-        dpv[4 * g + 3] = -d4.w;
-      }
+      for (int rr = 0; rr < 16; ++rr) s[rr] = dpv[rr] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(qn, 2 * ks + sb), kb[ks], s, 0, 0,
@@ -557,20 +550,34 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
                                                       0, 0);
       }
     };
+    // tile row r is token tq0 + r / G: it precedes this lane's key exactly
+    // when r < (key - tq0) * G
+    const int lim = (int)min(max(key - tq0, (int64_t)-1), (int64_t)QROWS) * G - 4 * lh;
     auto causal = [&](int sb, floatx16 &s) {
       if (masked) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int row = 32 * sb + 8 * (rr >> 2) + 4 * lh + (rr & 3);
-          const int64_t tk = tq0 + (int64_t)((row + 0.5f) * (1.0f / (float)G));
-          if (tk < key) s[rr] = -INFINITY;
-        }
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * sb + 8 * (rr >> 2) + (rr & 3) < lim) s[rr] = -INFINITY;
       }
     };
     // P and dS = P (dP - D) as bf16 B operands (k-step kk holds registers 8kk .. 8kk+7)
-    auto weights = [&](floatx16 &s, const floatx16 &dpv, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+    auto weights = [&](int sb, floatx16 &s, const floatx16 &dpv, bf16x8 (&pb)[2],
+                       bf16x8 (&dsb)[2]) {
+      floatx16 dd;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[rr] = fast_exp2(c * s[rr]);
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = 32 * sb + 8 * g + 4 * lh;
+        const float4 l4 = *(const float4 *)&lse_s[P][row0];
+        const float4 d4 = *(const float4 *)&del_s[P][row0];
+        s[4 * g + 0] = fast_exp2(fmaf(c, s[4 * g + 0], l4.x));
+        s[4 * g + 1] = fast_exp2(fmaf(c, s[4 * g + 1], l4.y));
+        s[4 * g + 2] = fast_exp2(fmaf(c, s[4 * g + 2], l4.z));
+        s[4 * g + 3] = fast_exp2(fmaf(c, s[4 * g + 3], l4.w));
+        dd[4 * g + 0] = dpv[4 * g + 0] + d4.x;
+        dd[4 * g + 1] = dpv[4 * g + 1] + d4.y;
+        dd[4 * g + 2] = dpv[4 * g + 2] + d4.z;
+        dd[4 * g + 3] = dpv[4 * g + 3] + d4.w;
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 w, wd;
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int rr = 8 * kk + 2 * q;
           w[q] = cvt_bf16x2(s[rr], s[rr + 1]);
-          wd[q] = cvt_bf16x2(s[rr] * dpv[rr], s[rr + 1] * dpv[rr + 1]);
+          wd[q] = cvt_bf16x2(s[rr] * dd[rr], s[rr + 1] * dd[rr + 1]);
         }
         pb[kk] = __builtin_bit_cast(bf16x8, w);
         dsb[kk] = __builtin_bit_cast(bf16x8, wd);
@@ -605,17 +612,14 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     causal(0, s0);
     scores(1, s1, d1);
     bf16x8 pb0[2], ds0[2];
-    weights(s0, d0, pb0, ds0);
+    weights(0, s0, d0, pb0, ds0);
     causal(1, s1);
     grads(0, pb0, ds0);
     bf16x8 pb1[2], ds1[2];
-    weights(s1, d1, pb1, ds1);
+    weights(1, s1, d1, pb1, ds1);
     grads(1, pb1, ds1);
     wait_vmem();
-    if (more && wave == 0) {
-      lse_s[P ^ 1][lane] = l2n;
-      del_s[P ^ 1][lane] = dln;
-    }
+    if (more && wave == 0) store_stats(P ^ 1, rn);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
