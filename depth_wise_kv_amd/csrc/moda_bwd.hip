@@ -19,11 +19,13 @@
 //                   walks the key tiles up to the diagonal.  Per tile:
 //                   S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T,
 //                   all on v_mfma_f32_32x32x16_bf16 with a lane owning a row.
-//   moda_bwd_dkdv   dK, dV.  A workgroup owns 128 sequence keys (4 waves x 32)
-//                   and walks the query tiles of 64 rows (64/G tokens x G
-//                   heads) from its first key to the end.  Per tile and
-//                   32-row block: S = Q K^T, P, dP = dO V^T, dS,
-//                   dV^T += dO^T P, dK^T += Q^T dS, with a lane owning a key.
+//   moda_bwd_dkdv   dK, dV.  A workgroup owns 128 sequence keys (4 groups of
+//                   32, a lane per key) and walks the query tiles of 64 rows
+//                   (64/G tokens x G heads) from its first key to the end.
+//                   Each group has two waves on one SIMD: one computes
+//                   S = Q K^T and P and accumulates dV^T += dO^T P; the other
+//                   computes dP = dO V^T, takes P through LDS after a
+//                   mid-tile barrier, and accumulates dK^T += Q^T dS.
 // The key and query tiles go from global memory straight into LDS.  Each
 // tile is stored twice where it is read both ways: "row-swizzled" (chunk c
 // of row r in slot c ^ (r % 16), for operands that hold 8 dims of one row)
@@ -390,13 +392,14 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 sequence keys, query tiles of 64 rows.
+// dK, dV: 4 key groups x 32 sequence keys; query tiles of 64 rows.  Each key
+// group has two waves on one SIMD: one computes S and P and accumulates dV,
+// the other computes dP, takes P from the first through LDS, and accumulates
+// dK.
 // ---------------------------------------------------------------------------
-#ifndef MODA_BWD_KV_WAVES
-#define MODA_BWD_KV_WAVES 4
-#endif
-constexpr int KV_WAVES = MODA_BWD_KV_WAVES;
-constexpr int KV_KEYS = 32 * KV_WAVES;
+constexpr int KV_GROUPS = 4;             // key groups of 32 per workgroup
+constexpr int KV_WAVES = 2 * KV_GROUPS;  // a dV wave and a dK wave per group
+constexpr int KV_KEYS = 32 * KV_GROUPS;
 constexpr int QROWS = 64;
 constexpr int KV_ROWS = QROWS / KV_WAVES;  // query tile rows each wave loads
 constexpr int KV_DMA = KV_ROWS / 4;        // 4-row load instructions per copy
@@ -420,12 +423,18 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char rg1[BTILE];
   __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];  // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];  // -D
+  // P of the tile as the dV wave's bf16 B operands: [group][block][k-step][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 p_x[KV_GROUPS][2][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lh = lane >> 5;
   const TileFrags fr(lane);
+  // waves kg and kg + 4 share a SIMD and the key group kg: the first
+  // accumulates dV (from S and P), the second dK (from S, dP and dS)
+  const int kg = wave % KV_GROUPS;
+  const bool dk_wave = wave >= KV_GROUPS;
 
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
@@ -435,18 +444,19 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int64_t k0 = ktile * KV_KEYS;
 
-  // this lane's key (the column of every product) and its K, V rows as B operands
-  const int64_t key = k0 + 32 * wave + li;
+  // this lane's key (the column of every product) and its K row (dV wave) or
+  // V row (dK wave) as B operands
+  const int64_t key = k0 + 32 * kg + li;
   const bool key_ok = key < T;
-  bf16x8 kb[8], vb[8];
-  load_row_operand((const __bf16 *)p.k + (bh * T + (key_ok ? key : 0)) * BD, key_ok, lh, kb);
-  load_row_operand((const __bf16 *)p.v + (bh * T + (key_ok ? key : 0)) * BD, key_ok, lh, vb);
+  const int64_t krow = bh * T + (key_ok ? key : 0);
+  bf16x8 kvb[8];
+  load_row_operand((const __bf16 *)(dk_wave ? p.v : p.k) + krow * BD, key_ok, lh, kvb);
 
-  floatx16 dk[4], dv[4];
+  floatx16 acc[4];  // dV^T or dK^T of the 32 keys
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) dk[nb][rr] = dv[nb][rr] = 0.f;
+    for (int rr = 0; rr < 16; ++rr) acc[nb][rr] = 0.f;
 
   const float c = p.scale_log2;
   // query tiles: tokens from k0 (the first that sees a key of this workgroup)
@@ -524,8 +534,9 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   __syncthreads();
 
   // query tile qt in buffers of parity P; loads of tile qt+1 are issued first
-  auto body = [&](int64_t qt, auto parity) {
+  auto body = [&](int64_t qt, auto parity, auto is_dk) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
+    constexpr bool DK = decltype(is_dk)::value;
     const char *const qn = P ? rq1 : rq0;
     const char *const qtr = P ? cq1 : cq0;
     const char *const gn = P ? rg1 : rg0;
@@ -535,106 +546,113 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     const RowStats rn = row_stats(qt + 1);
     const int64_t tq0 = k0 + qt * TQr;  // first token of the tile
     // the tile needs the causal mask unless its first token is at or past
-    // this wave's last key
-    const bool masked = tq0 < k0 + 32 * wave + 31;
-    // register rr of a 32-row block sb holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4.
-    // S = Q K^T and dP = dO V^T (rows x keys): two independent MFMA chains, interleaved
-    auto scores = [&](int sb, floatx16 &s, floatx16 &dpv) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s[rr] = dpv[rr] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(qn, 2 * ks + sb), kb[ks], s, 0, 0,
-                                                    0);
-        dpv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(gn, 2 * ks + sb), vb[ks], dpv, 0,
-                                                      0, 0);
-      }
-    };
+    // this group's last key
+    const bool masked = tq0 < k0 + 32 * kg + 31;
     // tile row r is token tq0 + r / G: it precedes this lane's key exactly
     // when r < (key - tq0) * G
     const int lim = (int)min(max(key - tq0, (int64_t)-1), (int64_t)QROWS) * G - 4 * lh;
-    auto causal = [&](int sb, floatx16 &s) {
-      if (masked) {
+    // register rr of 32-row block sb holds tile row 32*sb + 8*(rr/4) + 4*lh + rr%4.
+    // Phase 1: S = Q K^T and P (dV wave, P also to LDS), dP = dO V^T (dK wave)
+    floatx16 x[2];
+    bf16x8 wb[2][2];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (32 * sb + 8 * (rr >> 2) + (rr & 3) < lim) s[rr] = -INFINITY;
-      }
-    };
-    // P and dS = P (dP - D) as bf16 B operands (k-step kk holds registers 8kk .. 8kk+7)
-    auto weights = [&](int sb, floatx16 &s, const floatx16 &dpv, bf16x8 (&pb)[2],
-                       bf16x8 (&dsb)[2]) {
-      floatx16 dd;
+    for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row0 = 32 * sb + 8 * g + 4 * lh;
-        const float4 l4 = *(const float4 *)&lse_s[P][row0];
-        const float4 d4 = *(const float4 *)&del_s[P][row0];
-        s[4 * g + 0] = fast_exp2(fmaf(c, s[4 * g + 0], l4.x));
-        s[4 * g + 1] = fast_exp2(fmaf(c, s[4 * g + 1], l4.y));
-        s[4 * g + 2] = fast_exp2(fmaf(c, s[4 * g + 2], l4.z));
-        s[4 * g + 3] = fast_exp2(fmaf(c, s[4 * g + 3], l4.w));
-        dd[4 * g + 0] = dpv[4 * g + 0] + d4.x;
-        dd[4 * g + 1] = dpv[4 * g + 1] + d4.y;
-        dd[4 * g + 2] = dpv[4 * g + 2] + d4.z;
-        dd[4 * g + 3] = dpv[4 * g + 3] + d4.w;
-      }
+      for (int rr = 0; rr < 16; ++rr) x[sb][rr] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 w, wd;
+      for (int ks = 0; ks < 8; ++ks)
+        x[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.rowfrag(DK ? gn : qn, 2 * ks + sb),
+                                                        kvb[ks], x[sb], 0, 0, 0);
+    }
+    if constexpr (DK) {
+      // dP - D, ahead of the barrier
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int rr = 8 * kk + 2 * q;
-          w[q] = cvt_bf16x2(s[rr], s[rr + 1]);
-          wd[q] = cvt_bf16x2(s[rr] * dd[rr], s[rr + 1] * dd[rr + 1]);
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 d4 = *(const float4 *)&del_s[P][32 * sb + 8 * g + 4 * lh];
+          x[sb][4 * g + 0] += d4.x;
+          x[sb][4 * g + 1] += d4.y;
+          x[sb][4 * g + 2] += d4.z;
+          x[sb][4 * g + 3] += d4.w;
         }
-        pb[kk] = __builtin_bit_cast(bf16x8, w);
-        dsb[kk] = __builtin_bit_cast(bf16x8, wd);
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (masked) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (32 * sb + 8 * (rr >> 2) + (rr & 3) < lim) x[sb][rr] = -INFINITY;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *(const float4 *)&lse_s[P][32 * sb + 8 * g + 4 * lh];
+          x[sb][4 * g + 0] = fast_exp2(fmaf(c, x[sb][4 * g + 0], l4.x));
+          x[sb][4 * g + 1] = fast_exp2(fmaf(c, x[sb][4 * g + 1], l4.y));
+          x[sb][4 * g + 2] = fast_exp2(fmaf(c, x[sb][4 * g + 2], l4.z));
+          x[sb][4 * g + 3] = fast_exp2(fmaf(c, x[sb][4 * g + 3], l4.w));
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            u[q] = cvt_bf16x2(x[sb][8 * kk + 2 * q], x[sb][8 * kk + 2 * q + 1]);
+          wb[sb][kk] = __builtin_bit_cast(bf16x8, u);
+          p_x[kg][sb][kk][lane] = wb[sb][kk];
+        }
       }
-    };
-    // dV^T += dO^T P ; dK^T += Q^T dS  (k-steps 2*sb + kk of the tile)
-    auto grads = [&](int sb, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+    }
+    __syncthreads();
+    // Phase 2: dV^T += dO^T P (dV wave); dS = P (dP - D), dK^T += Q^T dS (dK wave)
+    if constexpr (DK) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const floatx16 &d = x[sb];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 pw = __builtin_bit_cast(u32x4, p_x[kg][sb][kk][lane]);
+          u32x4 u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = 8 * kk + 2 * q;
+            u[q] = cvt_bf16x2(bf16_bits_to_float(pw[q] & 0xFFFFu) * d[rr],
+                              bf16_bits_to_float(pw[q] >> 16) * d[rr + 1]);
+          }
+          wb[sb][kk] = __builtin_bit_cast(bf16x8, u);
+        }
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(gtr, 4 * nb + 2 * sb + kk),
-                                                           pb[kk], dv[nb], 0, 0, 0);
-          dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(qtr, 4 * nb + 2 * sb + kk),
-                                                           dsb[kk], dk[nb], 0, 0, 0);
-        }
-    };
-    // Two-stage pipeline over the tile's two 32-row blocks: block 1's score
-    // MFMAs are issued before block 0's exponentials, and block 0's gradient
-    // MFMAs before block 1's, so the matrix core runs while the wave's own
-    // VALU works (one wave per SIMD: no other wave fills those gaps).
-    floatx16 s0, d0, s1, d1;
-    scores(0, s0, d0);
-    causal(0, s0);
-    scores(1, s1, d1);
-    bf16x8 pb0[2], ds0[2];
-    weights(0, s0, d0, pb0, ds0);
-    causal(1, s1);
-    grads(0, pb0, ds0);
-    bf16x8 pb1[2], ds1[2];
-    weights(1, s1, d1, pb1, ds1);
-    grads(1, pb1, ds1);
+        for (int nb = 0; nb < 4; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              fr.colfrag(DK ? qtr : gtr, 4 * nb + 2 * sb + kk), wb[sb][kk], acc[nb], 0, 0, 0);
     wait_vmem();
     if (more && wave == 0) store_stats(P ^ 1, rn);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int64_t qt = 0;
-  for (; qt + 1 < n_qt; qt += 2) {
-    body(qt, I0{});
-    body(qt + 1, I1{});
-  }
-  if (qt < n_qt) body(qt, I0{});
+  auto run = [&](auto is_dk) __attribute__((always_inline)) {
+    int64_t qt = 0;
+    for (; qt + 1 < n_qt; qt += 2) {
+      body(qt, I0{}, is_dk);
+      body(qt + 1, I1{}, is_dk);
+    }
+    if (qt < n_qt) body(qt, I0{}, is_dk);
+  };
+  if (dk_wave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
-  if (key_ok) {
-    store_row((__bf16 *)p.dk + (bh * T + key) * BD, dk, p.scale, lh);
-    store_row((__bf16 *)p.dv + (bh * T + key) * BD, dv, 1.0f, lh);
-  }
+  if (key_ok)
+    store_row((__bf16 *)(dk_wave ? p.dk : p.dv) + (bh * T + key) * BD, acc,
+              dk_wave ? p.scale : 1.0f, lh);
 }
 
 // ---------------------------------------------------------------------------
