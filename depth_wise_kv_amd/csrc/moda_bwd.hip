@@ -14,11 +14,12 @@
 //
 // Kernels:
 //   moda_bwd_delta  D for every query row.
-//   moda_bwd_dq     dQ.  A workgroup owns 256 query rows (the forward's
-//                   tiling: 256/G tokens x the G heads of one KV group) and
-//                   walks the key tiles up to the diagonal.  Per tile:
-//                   S^T = K Q^T, P^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T,
-//                   all on v_mfma_f32_32x32x16_bf16 with a lane owning a row.
+//   moda_bwd_dq     dQ over the sequence keys.  A workgroup owns 256 query
+//                   rows (the forward's tiling: 256/G tokens x the G heads of
+//                   one KV group) and walks the key tiles up to the diagonal.
+//                   Per tile: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
+//                   dQ^T += K^T dS^T, all on v_mfma_f32_32x32x16_bf16 with a
+//                   lane owning a row.
 //   moda_bwd_dkdv   dK, dV.  A workgroup owns 128 sequence keys (4 groups of
 //                   32, a lane per key) and walks the query tiles of 64 rows
 //                   (64/G tokens x G heads) from its first key to the end.
@@ -26,6 +27,10 @@
 //                   S = Q K^T and P and accumulates dV^T += dO^T P; the other
 //                   computes dP = dO V^T, takes P through LDS after a
 //                   mid-tile barrier, and accumulates dK^T += Q^T dS.
+//   moda_bwd_ddepth dKd, dVd, and the depth entries' part of dQ (added to
+//                   the sequence part dq wrote): each span of whole tokens
+//                   has a wave per entry orientation and a wave per row
+//                   orientation reading the same depth blocks.
 // The key and query tiles go from global memory straight into LDS.  Each
 // tile is stored twice where it is read both ways: "row-swizzled" (chunk c
 // of row r in slot c ^ (r % 16), for operands that hold 8 dims of one row)
@@ -107,7 +112,6 @@ __global__ __launch_bounds__(256) void moda_bwd_delta(BwdArgs p) {
 constexpr int DQ_WAVES = 8;
 constexpr int DQ_ROWS = 32 * DQ_WAVES;  // 256
 
-template <bool HAS_DEPTH>
 __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = DQ_ROWS / G;
@@ -289,103 +293,6 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   for (; j < n_kt; ++j) {
     if (j & 1) body(j, I1{}, j >= n_nm);
     else body(j, I0{}, j >= n_nm);
-  }
-
-  // ---------------- depth part of dQ: this wave's tokens' depth entries.
-  // Per 32-entry block: S_d^T = Kd Q^T (packed K half), P_d^T, dP_d^T = Vd dO^T
-  // (natural Vd rows), dS_d^T, then dQ^T += Kd^T dS_d^T with Kd^T read
-  // transposed from the block's natural Kd rows, loaded into this wave's
-  // 8 KiB of the (now idle) tile buffers.  Entries of other tokens in a block
-  // get weight 0.
-  if constexpr (HAS_DEPTH) {
-    const int64_t L = p.L;
-    const int64_t wt_lo = t0 + (wave * 32) / G;
-    int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;
-    if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
-    if (wt_hi > T) wt_hi = T;
-    if (L > 0 && wt_lo < wt_hi) {
-      const int64_t TL = T * L;
-      const int64_t blk_lo = (wt_lo * L) / kDepthBlock;
-      const int64_t blk_hi = (wt_hi * L + kDepthBlock - 1) / kDepthBlock;
-      char *const slot = (wave < 2 ? kn0 : wave < 4 ? kn1 : wave < 6 ? kt0 : kt1) +
-                         (wave & 1) * (BTILE / 2);
-      const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
-      const __bf16 *vnat = (const __bf16 *)p.vd + bh * TL * BD;
-      const __amdgpu_buffer_rsrc_t kd_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)((const char *)p.kd + bh * TL * (BD * 2)), (short)0, (int)(TL * (BD * 2)),
-          0x00020000);
-      const int64_t my_lo = tok * L;
-      for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
-        // natural Kd rows of the block into the slot, column-swizzled
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot's last reads are done
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = 4 * i + (lane >> 4);
-          dma16(kd_rsrc, slot + 4 * i * 256,
-                (uint32_t)(row * 256 + 16 * col_swz(row, lane & 15)),
-                (uint32_t)(blk * kDepthBlock * 256));
-        }
-        // S_d^T from the packed K half
-        floatx16 sd;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sd[rr] = init_s;
-        {
-          u32x4 kd[8];
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]),
-                                                         qb[ks], sd, 0, 0, 0);
-        }
-        // register rr holds entry blk*32 + 8*(rr/4) + 4*lh + rr%4: keep it iff
-        // it is one of this row's token's entries
-        {
-          const int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
-          const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[rr] = -INFINITY;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sd[rr] = fast_exp2(c * sd[rr]);
-        // dP_d^T = Vd dO^T - D from the natural Vd rows (entry lane%32)
-        floatx16 dpd;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) dpd[rr] = init_dp;
-        {
-          const int64_t e = blk * kDepthBlock + li;
-          const bool e_ok = e < TL;
-          u32x4 vr[8];
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            vr[ks] = e_ok ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[ks]),
-                                                          gb[ks], dpd, 0, 0, 0);
-        }
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          u32x4 w;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rr = 8 * kk + 2 * q;
-            w[q] = cvt_bf16x2(sd[rr] * dpd[rr], sd[rr + 1] * dpd[rr + 1]);
-          }
-          dsb[kk] = __builtin_bit_cast(bf16x8, w);
-        }
-        wait_vmem();  // the Kd rows have landed in the slot
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb + kk),
-                                                             dsb[kk], dq[nb], 0, 0, 0);
-      }
-    }
   }
 
   if (row_ok) store_row((__bf16 *)p.dq + qrow * BD, dq, p.scale, lh);
@@ -656,25 +563,40 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// dKd, dVd: depth entries' gradients.  8 waves; a wave owns TW = floor(32/G)
-// whole tokens (their G query rows each), so every row that reads an entry
-// is in the entry's wave.  Per 32-entry block of the wave's span, with a lane
-// owning an entry: S_d = Q Kd^T (packed K half), P_d, dP_d = dO Vd^T (natural
-// Vd rows), dS_d; dVd^T = dO^T P_d and dKd^T = Q^T dS_d with Q^T and dO^T read
-// transposed from this wave's own rows, stored once in LDS.
+// Depth gradients: dKd, dVd and the depth entries' part of dQ.  A workgroup
+// covers DD_SPANS spans of TW = floor(32/G) whole tokens (their G query rows
+// each, 32 rows at most), with two waves per span on one SIMD:
+//   the entry wave (a lane per entry of a 32-entry block): S_d = Q Kd^T, P_d,
+//     dP_d = dO Vd^T, dS_d; dVd^T = dO^T P_d and dKd^T = Q^T dS_d, with Q^T
+//     and dO^T read transposed from the span's rows stored once in LDS;
+//   the row wave (a lane per query row): S_d^T = Kd Q^T, P_d^T,
+//     dP_d^T = Vd dO^T, dS_d^T; dQ^T += Kd^T dS_d^T, with Kd^T read
+//     transposed from the block's K rows, which the wave copies from its
+//     registers into LDS; at the end it adds the sum to dQ, which holds the
+//     sequence part.
+// Both waves read the same blocks (packed K half, natural Vd rows) at about
+// the same time, so the second read is served by L2.  Every row that reads
+// an entry is in the entry's span, so no atomics are needed.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
+constexpr int DD_SPANS = 4;
+constexpr int DD_WAVES = 2 * DD_SPANS;
+
+__global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
-  const int TW = 32 / G;            // tokens per wave (G <= 32)
-  const int TWG = TW * DQ_WAVES;    // tokens per workgroup
-  __shared__ __attribute__((aligned(1024))) char q_s[DQ_WAVES][32 * 256];
-  __shared__ __attribute__((aligned(1024))) char g_s[DQ_WAVES][32 * 256];
-  __shared__ __attribute__((aligned(16))) float lse_s[DQ_WAVES][32];
-  __shared__ __attribute__((aligned(16))) float del_s[DQ_WAVES][32];
+  const int TW = 32 / G;            // tokens per span (G <= 32)
+  const int TWG = TW * DD_SPANS;    // tokens per workgroup
+  __shared__ __attribute__((aligned(1024))) char q_s[DD_SPANS][32 * 256];
+  __shared__ __attribute__((aligned(1024))) char g_s[DD_SPANS][32 * 256];
+  __shared__ __attribute__((aligned(1024))) char k_s[DD_SPANS][32 * 256];
+  __shared__ __attribute__((aligned(16))) float lse_s[DD_SPANS][32];  // -lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float del_s[DD_SPANS][32];  // -D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // waves s and s + DD_SPANS share a SIMD and span s
+  const int span = wave % DD_SPANS;
+  const bool row_wave = wave >= DD_SPANS;
   const int li = lane & 31, lh = lane >> 5;
   const TileFrags fr(lane);
 
@@ -683,11 +605,11 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   const int64_t x = blockIdx.x;
   const int64_t bh = x % BH;
   const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
-  const int64_t wt_lo = (x / BH) * TWG + (int64_t)wave * TW;  // this wave's first token
+  const int64_t wt_lo = (x / BH) * TWG + (int64_t)span * TW;  // the span's first token
   int64_t wt_hi = wt_lo + TW;
   if (wt_hi > T) wt_hi = T;
 
-  // this lane's row (as an A operand and for the LDS copies): row li
+  // this lane's row: an MFMA operand of either wave, and the LDS copies
   const int r = li;
   const bool row_used = r < TW * G;
   const int64_t tok = wt_lo + r / G;
@@ -697,113 +619,192 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   bf16x8 qb[8], gb[8];
   load_row_operand((const __bf16 *)p.q + qrow * BD, row_ok, lh, qb);
   load_row_operand((const __bf16 *)p.dout + qrow * BD, row_ok, lh, gb);
-  // the wave's rows into LDS, column-swizzled, for the transposed products
-  char *const qs = q_s[wave];
-  char *const gs = g_s[wave];
+  // rows outside the problem get weight 0
+  const float l_row = row_ok ? -LOG2E * p.lse[qrow] : -INFINITY;
+  const float d_row = row_ok ? -p.delta[qrow] : 0.f;
+  if (!row_wave) {
+    char *const qs = q_s[span];
+    char *const gs = g_s[span];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int chunk = 8 * lh + ks;
-    const int off = r * 256 + 16 * (chunk ^ (4 * (r & 3)));
-    *(bf16x8 *)(qs + off) = qb[ks];
-    *(bf16x8 *)(gs + off) = gb[ks];
-  }
-  if (lh == 0) {
-    lse_s[wave][r] = row_ok ? p.lse[qrow] * LOG2E : INFINITY;
-    del_s[wave][r] = row_ok ? p.delta[qrow] : 0.f;
+    for (int ks = 0; ks < 8; ++ks) {
+      const int off = r * 256 + 16 * col_swz(r, 8 * lh + ks);
+      *(bf16x8 *)(qs + off) = qb[ks];
+      *(bf16x8 *)(gs + off) = gb[ks];
+    }
+    if (lh == 0) {
+      lse_s[span][r] = l_row;
+      del_s[span][r] = d_row;
+    }
   }
   __syncthreads();
   if (wt_lo >= T) return;
 
   const float c = p.scale_log2;
-  const float neg_inv_c = -1.0f / c;
-  const int64_t e_lo = wt_lo * L, e_hi = wt_hi * L;  // entries this wave owns
+  const int64_t e_lo = wt_lo * L, e_hi = wt_hi * L;  // entries of the span's tokens
   const int64_t blk_lo = e_lo / kDepthBlock;
   const int64_t blk_hi = (e_hi + kDepthBlock - 1) / kDepthBlock;
-  const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
-  const __bf16 *vnat = (const __bf16 *)p.vd + bh * TL * BD;
-  // register rr of a block holds row 8*(rr/4) + 4*lh + rr%4; its lse2 and D
-  // are read from LDS when needed
-  auto row_init = [&](const float (*buf)[32], float mul, floatx16 &acc) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 v4 = *(const float4 *)&buf[wave][8 * g + 4 * lh];
-      acc[4 * g + 0] = v4.x * mul;
-      acc[4 * g + 1] = v4.y * mul;
-      acc[4 * g + 2] = v4.z * mul;
-      acc[4 * g + 3] = v4.w * mul;
-    }
-  };
-  const int tw_rows = TW * G;
-
-  for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
-    const int64_t e = blk * kDepthBlock + li;  // this lane's entry
-    // S_d = Q Kd^T (rows x entries)
-    floatx16 sd;
-    row_init(lse_s, neg_inv_c, sd);
-    // the block's Kd rows (packed K half) and Vd rows (natural): all sixteen
-    // loads in flight before the first MFMA waits
-    u32x4 kd[8], vr[8];
+  const char *const pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
+  const __bf16 *const vnat = (const __bf16 *)p.vd + bh * TL * BD;
+  // the block's Kd rows (packed K half: lane = entry, 8 dims a k-step) and Vd
+  // rows (natural) as MFMA operands; the sixteen loads go out together
+  auto load_block = [&](int64_t blk, u32x4 (&kd)[8], u32x4 (&vr)[8]) {
+    const int64_t e = blk * kDepthBlock + li;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       vr[ks] = e < TL ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
-    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (!row_wave) {
+    const char *const qs = q_s[span];
+    const char *const gs = g_s[span];
+    for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+      const int64_t e = blk * kDepthBlock + li;  // this lane's entry
+      u32x4 kd[8], vr[8];
+      load_block(blk, kd, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      // S_d = Q Kd^T and dP_d = dO Vd^T (rows x entries)
+      floatx16 sd, dpd;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]), sd,
-                                                   0, 0, 0);
-    // keep (row, entry) iff the entry is one of the row's token's entries
-    const int64_t etok = e / L - wt_lo;  // the entry's token, relative
+      for (int rr = 0; rr < 16; ++rr) sd[rr] = dpd[rr] = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int row = 8 * (rr >> 2) + 4 * lh + (rr & 3);
-      if (row >= tw_rows || (int64_t)(row / G) != etok || e >= e_hi) sd[rr] = -INFINITY;
+      for (int ks = 0; ks < 8; ++ks) {
+        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]),
+                                                     sd, 0, 0, 0);
+        dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
+                                                      dpd, 0, 0, 0);
+      }
+      // register rr holds row 8*(rr/4) + 4*lh + rr%4: keep it iff the row is
+      // one of the G rows of the entry's token, i.e. row - etok*G in [0, G)
+      const int etok = (int)(e / L - wt_lo);
+      const int base = 4 * lh - etok * G;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if ((unsigned)(8 * (rr >> 2) + (rr & 3) + base) >= (unsigned)G) sd[rr] = -INFINITY;
+      // P_d and dS_d = P_d (dP_d - D) as bf16 B operands
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const float4 la = *(const float4 *)&lse_s[span][8 * (2 * kk) + 4 * lh];
+        const float4 lb = *(const float4 *)&lse_s[span][8 * (2 * kk + 1) + 4 * lh];
+        const float4 da = *(const float4 *)&del_s[span][8 * (2 * kk) + 4 * lh];
+        const float4 db = *(const float4 *)&del_s[span][8 * (2 * kk + 1) + 4 * lh];
+        const float lr[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const float dr[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+        u32x4 w, wd;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 8 * kk + 2 * q;
+          const float p0 = fast_exp2(fmaf(c, sd[rr], lr[2 * q]));
+          const float p1 = fast_exp2(fmaf(c, sd[rr + 1], lr[2 * q + 1]));
+          w[q] = cvt_bf16x2(p0, p1);
+          wd[q] = cvt_bf16x2(p0 * (dpd[rr] + dr[2 * q]), p1 * (dpd[rr + 1] + dr[2 * q + 1]));
+        }
+        pb[kk] = __builtin_bit_cast(bf16x8, w);
+        dsb[kk] = __builtin_bit_cast(bf16x8, wd);
+      }
+      // dVd^T = dO^T P_d, then dKd^T = Q^T dS_d (the span's 32 rows as two
+      // k-steps), one accumulator set at a time
+      const bool owned = e >= e_lo && e < e_hi;
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        floatx16 acc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) acc[nb][rr] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fr.colfrag(which ? qs : gs, 4 * nb + kk), which ? dsb[kk] : pb[kk], acc[nb], 0,
+                0, 0);
+        if (owned)
+          store_row((__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + e) * BD, acc,
+                    which ? p.scale : 1.0f, lh);
+      }
     }
+    return;
+  }
+
+  // row wave
+  char *const ks_ = k_s[span];
+  floatx16 dq[4];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sd[rr] = fast_exp2(c * sd[rr]);
-    // dP_d = dO Vd^T - D
-    floatx16 dpd;
-    row_init(del_s, -1.0f, dpd);
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) dq[nb][rr] = 0.f;
+  const int64_t my_lo = tok * L;  // this row's token's first entry
+  for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+    u32x4 kd[8], vr[8];
+    load_block(blk, kd, vr);
+    __builtin_amdgcn_sched_barrier(0);
+    // the block's K rows into LDS, column-swizzled, for the transposed product
+    // (LDS operations of one wave run in order: the last block's reads are done)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
-                                                    dpd, 0, 0, 0);
-    bf16x8 pb[2], dsb[2];
+      *(u32x4 *)(ks_ + li * 256 + 16 * col_swz(li, 8 * lh + ks)) = kd[ks];
+    // S_d^T = Kd Q^T and dP_d^T = Vd dO^T (entries x rows)
+    floatx16 st, dpt;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) st[rr] = dpt[rr] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]), qb[ks], st,
+                                                   0, 0, 0);
+      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[ks]), gb[ks],
+                                                    dpt, 0, 0, 0);
+    }
+    // register rr holds entry blk*32 + 8*(rr/4) + 4*lh + rr%4: keep it iff it
+    // is one of this row's token's entries
+    {
+      const int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
+      const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) st[rr] = -INFINITY;
+    }
+    // dS_d^T = P_d^T (dP_d^T - D) as bf16 B operands
+    bf16x8 dsb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4 w, wd;
+      u32x4 w;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rr = 8 * kk + 2 * q;
-        w[q] = cvt_bf16x2(sd[rr], sd[rr + 1]);
-        wd[q] = cvt_bf16x2(sd[rr] * dpd[rr], sd[rr + 1] * dpd[rr + 1]);
+        const float p0 = fast_exp2(fmaf(c, st[rr], l_row));
+        const float p1 = fast_exp2(fmaf(c, st[rr + 1], l_row));
+        w[q] = cvt_bf16x2(p0 * (dpt[rr] + d_row), p1 * (dpt[rr + 1] + d_row));
       }
-      pb[kk] = __builtin_bit_cast(bf16x8, w);
-      dsb[kk] = __builtin_bit_cast(bf16x8, wd);
+      dsb[kk] = __builtin_bit_cast(bf16x8, w);
     }
-    // dVd^T = dO^T P_d, then dKd^T = Q^T dS_d (the wave's 32 rows as two
-    // k-steps), one accumulator set at a time
-    const bool owned = e >= e_lo && e < e_hi;
+    // dQ^T += Kd^T dS_d^T over the block's 32 entries (two k-steps)
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      floatx16 acc[4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
+        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(ks_, 4 * nb + kk), dsb[kk],
+                                                         dq[nb], 0, 0, 0);
+  }
+  // dQ (the sequence part, as written) += s * the depth part
+  if (row_ok) {
+    __bf16 *const row = (__bf16 *)p.dq + qrow * BD;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[nb][rr] = 0.f;
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              fr.colfrag(which ? qs : gs, 4 * nb + kk), which ? dsb[kk] : pb[kk], acc[nb], 0, 0,
-              0);
-      if (owned)
-        store_row((__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + e) * BD, acc,
-                  which ? p.scale : 1.0f, lh);
-    }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 *const pp = (u32x2 *)(row + 32 * nb + 8 * g + 4 * lh);
+        const u32x2 o = *pp;
+        u32x2 n;
+        n[0] = cvt_bf16x2(bf16_bits_to_float(o[0] & 0xFFFFu) + dq[nb][4 * g + 0] * p.scale,
+                          bf16_bits_to_float(o[0] >> 16) + dq[nb][4 * g + 1] * p.scale);
+        n[1] = cvt_bf16x2(bf16_bits_to_float(o[1] & 0xFFFFu) + dq[nb][4 * g + 2] * p.scale,
+                          bf16_bits_to_float(o[1] >> 16) + dq[nb][4 * g + 3] * p.scale);
+        *pp = n;
+      }
   }
 }
 
@@ -813,16 +814,14 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(moda_bwd_delta, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, s, a);
   const int64_t tq = DQ_ROWS / G;
   const int64_t dq_grid = (a.T + tq - 1) / tq * a.B * a.Hkv;
-  if (a.L > 0)
-    hipLaunchKernelGGL(moda_bwd_dq<true>, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
-  else
-    hipLaunchKernelGGL(moda_bwd_dq<false>, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
+  hipLaunchKernelGGL(moda_bwd_dq, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
   const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv;
   hipLaunchKernelGGL(moda_bwd_dkdv, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
   if (a.L > 0) {
-    const int64_t twg = (32 / G) * DQ_WAVES;
+    // after dq: it adds the depth entries' part to dQ
+    const int64_t twg = (32 / G) * DD_SPANS;
     const int64_t dd_grid = (a.T + twg - 1) / twg * a.B * a.Hkv;
-    hipLaunchKernelGGL(moda_bwd_ddepth, dim3((uint32_t)dd_grid), dim3(64 * DQ_WAVES), 0, s, a);
+    hipLaunchKernelGGL(moda_bwd_ddepth, dim3((uint32_t)dd_grid), dim3(64 * DD_WAVES), 0, s, a);
   }
   return hipGetLastError();
 }
