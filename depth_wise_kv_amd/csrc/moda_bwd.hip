@@ -588,6 +588,7 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char q_s[DD_SPANS][32 * 256];
   __shared__ __attribute__((aligned(1024))) char g_s[DD_SPANS][32 * 256];
   __shared__ __attribute__((aligned(1024))) char k_s[DD_SPANS][32 * 256];
+  __shared__ __attribute__((aligned(1024))) char o_s[DD_SPANS][32 * 256];  // output staging
   __shared__ __attribute__((aligned(16))) float lse_s[DD_SPANS][32];  // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float del_s[DD_SPANS][32];  // -D
 
@@ -706,8 +707,10 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
         dsb[kk] = __builtin_bit_cast(bf16x8, wd);
       }
       // dVd^T = dO^T P_d, then dKd^T = Q^T dS_d (the span's 32 rows as two
-      // k-steps), one accumulator set at a time
-      const bool owned = e >= e_lo && e < e_hi;
+      // k-steps), one accumulator set at a time.  Each goes to LDS as the
+      // block's 32 rows (chunk c of row r in slot c ^ (r % 16)) and from there
+      // to memory four whole rows per instruction.
+      char *const os = o_s[span];
 #pragma unroll
       for (int which = 0; which < 2; ++which) {
         floatx16 acc[4];
@@ -722,9 +725,24 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
             acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 fr.colfrag(which ? qs : gs, 4 * nb + kk), which ? dsb[kk] : pb[kk], acc[nb], 0,
                 0, 0);
-        if (owned)
-          store_row((__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + e) * BD, acc,
-                    which ? p.scale : 1.0f, lh);
+        const float sc = which ? p.scale : 1.0f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 o;
+            o[0] = cvt_bf16x2(acc[nb][4 * g + 0] * sc, acc[nb][4 * g + 1] * sc);
+            o[1] = cvt_bf16x2(acc[nb][4 * g + 2] * sc, acc[nb][4 * g + 3] * sc);
+            *(u32x2 *)(os + li * 256 + 16 * ((4 * nb + g) ^ (li & 15)) + 8 * lh) = o;
+          }
+        __bf16 *const dst = (__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + blk * kDepthBlock) * BD;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int rr = 4 * i + (lane >> 4), cc = lane & 15;
+          const u32x4 v = *(const u32x4 *)(os + rr * 256 + 16 * (cc ^ (rr & 15)));
+          const int64_t er = blk * kDepthBlock + rr;
+          if (er >= e_lo && er < e_hi) *(u32x4 *)(dst + rr * BD + 8 * cc) = v;
+        }
       }
     }
     return;
