@@ -64,6 +64,9 @@ def load(path: str | None = None):
     lib.oracle_depth_fwd.restype = ctypes.c_int
     lib.oracle_moda_bwd.argtypes = [i64] * 6 + [ctypes.c_int] + [vp] * 6 + [dp] * 5
     lib.oracle_moda_bwd.restype = ctypes.c_int
+    lib.oracle_moda_bwd_rows.argtypes = ([i64, vp] + [i64] * 6 + [ctypes.c_int] + [vp] * 6 +
+                                         [dp] * 3)
+    lib.oracle_moda_bwd_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
@@ -223,6 +226,40 @@ def moda_backward(q, k, v, kd, vd, dout, *, lib=None):
     if rc:
         raise ValueError(f"oracle_moda_bwd failed with code {rc}")
     return dq, dk, dv, dkd, dvd
+
+
+def moda_backward_rows(rows, shape, q_rows, dout_rows, k, v, kd_rows=None, vd_rows=None, *,
+                       lib=None):
+    """fp64 MoDA backward for selected rows only (the backward's per-row steps).
+
+    rows [R,3] int64 (b, h, t); shape = (B, Hq, Hkv, T, L, d); q_rows, dout_rows
+    [R,d]; k, v [B,Hkv,T,d]; kd_rows, vd_rows [R,L,d] (token t's depth rows of
+    each selected row).  Returns (dq [R,d], p [R,T+L], ds [R,T+L]) in float64:
+    the row's dQ, and its weight and softmax gradient for each entry it reads
+    (sequence keys 0..t, then depth entries at t+1+i; zero elsewhere).  dK_j is
+    then s * sum over the rows that read key j of ds[row, j] * q_row, and dV_j
+    the sum of p[row, j] * dout_row (likewise for the depth entries).
+    """
+    lib = lib or load()
+    B, Hq, Hkv, T, L, d = (int(x) for x in shape)
+    code = _code_of(q_rows)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    q_rows, dout_rows, k, v = (_as_input(x, code) for x in (q_rows, dout_rows, k, v))
+    if L:
+        kd_rows, vd_rows = _as_input(kd_rows, code), _as_input(vd_rows, code)
+        assert kd_rows.shape == (R, L, d) and vd_rows.shape == (R, L, d)
+    else:
+        kd_rows = vd_rows = None
+    dq = np.empty((R, d), np.float64)
+    p = np.empty((R, T + L), np.float64)
+    ds = np.empty((R, T + L), np.float64)
+    rc = lib.oracle_moda_bwd_rows(R, _ptr(rows), B, Hq, Hkv, T, L, d, code, _ptr(q_rows),
+                                  _ptr(dout_rows), _ptr(k), _ptr(v), _ptr(kd_rows),
+                                  _ptr(vd_rows), _ptr(dq), _ptr(p), _ptr(ds))
+    if rc:
+        raise ValueError(f"oracle_moda_bwd_rows failed with code {rc}")
+    return dq, p, ds
 
 
 def num_threads(*, lib=None) -> int:

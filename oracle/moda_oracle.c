@@ -366,3 +366,73 @@ int oracle_moda_bwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t L,
   }
   return fail ? 2 : 0;
 }
+
+/*
+ * The backward's per-row steps 7-10 and the dq_t of step 11 for selected rows
+ * only (the same calculus as oracle_moda_bwd, restricted to rows, for checks
+ * of large problems one row at a time).  The sums of step 11 over the rows
+ * that read a key are left to the caller, which gets each row's weights and
+ * ds over the entries it reads:
+ *   rows [R,3] (b, h, t); q_rows, dout_rows [R,d] in the input element type;
+ *   k, v [B,Hkv,T,d] full; kd_rows, vd_rows [R,L,d] (the row's token's depth
+ *   rows; NULL if L == 0)
+ *   dq_rows [R,d] double;
+ *   p, ds [R, T+L] double: entry n of row r at r*(T+L) + n, sequence keys
+ *   0..t first, then depth 0..L-1 at t+1+i; the rest of the row is zero.
+ */
+int oracle_moda_bwd_rows(int64_t R, const int64_t *rows, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t T, int64_t L, int64_t d, int dtype,
+                         const void *q_rows, const void *dout_rows, const void *k,
+                         const void *v, const void *kd_rows, const void *vd_rows,
+                         double *dq_rows, double *p, double *ds) {
+  if (bad_shape(B, Hq, Hkv, T, L, d, dtype) || R < 0) return 1;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t b = rows[3 * r], h = rows[3 * r + 1], t = rows[3 * r + 2];
+    if (b < 0 || b >= B || h < 0 || h >= Hq || t < 0 || t >= T) return 1;
+  }
+  const int64_t G = Hq / Hkv;
+  const int64_t W = T + L;
+  const double s = 1.0 / sqrt((double)d);
+  int fail = 0;
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)W * sizeof(double));
+    double *o = (double *)malloc((size_t)d * sizeof(double));
+    if (!x || !o) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t b = rows[3 * r], h = rows[3 * r + 1], t = rows[3 * r + 2];
+        const int64_t kv_off = (b * Hkv + h / G) * T * d;
+        const int64_t dep_off = r * L * d;
+        const int64_t n = t + 1 + L;
+        double *pr = p + r * W, *dsr = ds + r * W, *dqr = dq_rows + r * d;
+        /* step 7 */
+        moda_row(t, L, d, dtype, q_rows, r * d, k, v, kv_off, kd_rows, vd_rows, dep_off, o,
+                 NULL, x, NULL);
+        /* step 8 */
+        double D = 0.0;
+        for (int64_t c = 0; c < d; ++c) D += elem(dout_rows, r * d + c, dtype) * o[c];
+        for (int64_t c = 0; c < d; ++c) dqr[c] = 0.0;
+        for (int64_t nn = 0; nn < W; ++nn) pr[nn] = dsr[nn] = 0.0;
+        for (int64_t nn = 0; nn < n; ++nn) {
+          const int is_seq = nn <= t;
+          const void *key = is_seq ? k : kd_rows, *val = is_seq ? v : vd_rows;
+          const int64_t off = is_seq ? kv_off + nn * d : dep_off + (nn - t - 1) * d;
+          /* steps 9 and 10 */
+          const double dp = dot(dout_rows, r * d, val, off, d, dtype);
+          const double dsn = x[nn] * (dp - D);
+          pr[nn] = x[nn];
+          dsr[nn] = dsn;
+          /* step 11, dq_t */
+          for (int64_t c = 0; c < d; ++c) dqr[c] += s * dsn * elem(key, off + c, dtype);
+        }
+      }
+    }
+    free(x);
+    free(o);
+  }
+  return fail ? 2 : 0;
+}

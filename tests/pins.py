@@ -472,4 +472,38 @@ def pin_w_bwd_input_decoding(lib):
         assert np.array_equal(a, b), "bf16 decoding in the backward"
 
 
+def pin_x_bwd_rows_assemble(lib):
+    """The row-restricted backward, summed over every row that reads each key
+    (p * dO for values, s * ds * q for keys), rebuilds the full backward
+    (pinned above by finite differences and autograd), and its dQ rows match."""
+    for (B, Hq, Hkv, T, L, d, seed) in [(1, 4, 2, 6, 3, 8, 211), (2, 2, 1, 5, 0, 4, 212),
+                                        (1, 6, 2, 4, 2, 5, 213)]:
+        q, k, v, kd, vd, dout = _bwd_case(B, Hq, Hkv, T, L, d, seed)
+        want = _bwd(lib, q, k, v, kd, vd, dout)
+        G = Hq // Hkv
+        rows = np.array([(b, h, t) for b in range(B) for h in range(Hq) for t in range(T)],
+                        dtype=np.int64)
+        bi, hi, ti = rows[:, 0], rows[:, 1], rows[:, 2]
+        kd_rows = kd[bi, hi // G, ti] if L else None
+        vd_rows = vd[bi, hi // G, ti] if L else None
+        dq, p, ds = oracle.moda_backward_rows(rows, (B, Hq, Hkv, T, L, d), q[bi, hi, ti],
+                                              dout[bi, hi, ti], k, v, kd_rows, vd_rows, lib=lib)
+        s = 1.0 / math.sqrt(d)
+        dk, dv = np.zeros_like(k), np.zeros_like(v)
+        dkd = np.zeros_like(kd) if L else None
+        dvd = np.zeros_like(vd) if L else None
+        for r, (b, h, t) in enumerate(rows):
+            g = h // G
+            assert not np.any(p[r, t + 1 + L:]) and not np.any(ds[r, t + 1 + L:])
+            dk[b, g, :t + 1] += s * ds[r, :t + 1, None] * q[b, h, t]
+            dv[b, g, :t + 1] += p[r, :t + 1, None] * dout[b, h, t]
+            if L:
+                dkd[b, g, t] += s * ds[r, t + 1:t + 1 + L, None] * q[b, h, t]
+                dvd[b, g, t] += p[r, t + 1:t + 1 + L, None] * dout[b, h, t]
+        _close(dq.reshape(B, Hq, T, d), want[0], tol=1e-12, what="rows dq")
+        for name, got, ref in zip(("dk", "dv", "dkd", "dvd"), (dk, dv, dkd, dvd), want[1:]):
+            if ref is not None:
+                _close(got, ref, tol=1e-12, what=f"rows {name} {B,Hq,Hkv,T,L,d}")
+
+
 PINS = [(name, fn) for name, fn in sorted(globals().items()) if name.startswith("pin_")]

@@ -515,6 +515,111 @@ def test_bwd_parity(m, dev, B, Hq, Hkv, T, L):
     bwd_check(m, dev, B, Hq, Hkv, T, L, seed=300 + T + 7 * Hq)
 
 
+def bwd_sampled_check(m, cfg, dev, n_rows=16, n_tokens=4, n_end=3):
+    """The backward at a full workload size, launched as the bench times it.
+
+    Against the oracle's row-restricted backward: sampled dQ rows, every depth
+    entry of sampled tokens (dKd, dVd: all G rows of the token), and dK, dV of
+    the last n_end keys of one (b, kv head) (every row that reads them).  Over
+    all keys, the identity each row's weights (summing to one) give: per
+    (b, kv head) and dim, sum dV + sum dVd = sum of the group's dO rows.  (The
+    matching identity for keys, sum dK + sum dKd = 0, has no tolerance that
+    the device can compute and that is tight enough to catch a missing term,
+    so dK of the bulk of the keys is covered element by element at the 1.5B
+    layer's full size instead.)
+    """
+    import math
+    from gpu_util import to_np
+    from synth import bf16_bits_to_f32
+    B, Hq, Hkv, T, L, d = (cfg[x] for x in ("B", "Hq", "Hkv", "T", "L", "d"))
+    G = Hq // Hkv
+    s = 1.0 / math.sqrt(d)
+    d_in = device_case(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg["seed"] + 77)
+    dout = torch.randn((B, Hq, T, d), generator=gen, device=dev).to(torch.bfloat16)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"], m.make_shape(B, Hq, Hkv, T, L, d, "bf16"))
+    out, lse = m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
+    dq, dk, dv, dkd, dvd = m.bwd(d_in["q"], d_in["k"], d_in["v"], out, lse, dout, d_in["kd"],
+                                 d_in["vd"], packed)
+    torch.cuda.synchronize()
+    del out, lse, packed
+
+    rng = np.random.default_rng(cfg["seed"] + 78)
+    qrows = {(int(rng.integers(B)), int(rng.integers(Hq)), int(t))
+             for t in rng.integers(0, T, n_rows)} | {(0, 0, 0), (B - 1, Hq - 1, T - 1)}
+    toks = {(int(rng.integers(B)), int(rng.integers(Hkv)), int(t))
+            for t in rng.integers(0, T, n_tokens)} | {(0, 0, 0), (B - 1, Hkv - 1, T - 1)}
+    eb, eg = int(rng.integers(B)), int(rng.integers(Hkv))
+    need = set(qrows) | {(b, g * G + j, t) for b, g, t in toks for j in range(G)}
+    need |= {(eb, eg * G + j, t) for t in range(T - n_end, T) for j in range(G)}
+    rows = np.array(sorted(need), np.int64)
+    at = {tuple(r): i for i, r in enumerate(rows.tolist())}
+    rt = torch.from_numpy(rows).to(dev)
+    bi, hi, ti = rt[:, 0], rt[:, 1], rt[:, 2]
+    q_rows, do_rows = to_np(d_in["q"][bi, hi, ti]), to_np(dout[bi, hi, ti])
+    rdq, p, ds = oracle.moda_backward_rows(
+        rows, (B, Hq, Hkv, T, L, d), q_rows, do_rows, to_np(d_in["k"]), to_np(d_in["v"]),
+        to_np(d_in["kd"][bi, hi // G, ti]), to_np(d_in["vd"][bi, hi // G, ti]))
+    qf = bf16_bits_to_f32(q_rows).astype(np.float64)
+    df = bf16_bits_to_f32(do_rows).astype(np.float64)
+
+    def check(name, got, ref):
+        scale = max(1.0, float(np.max(np.abs(ref))))
+        e = max_err(got, ref)
+        print(f"[parity] bwd {cfg.get('name', '')} {name} max|err|={e:.3e} max|ref|={scale:.3e}",
+              flush=True)
+        assert e <= BWD_TOL * scale, f"{name}: {e} > {BWD_TOL} * {scale}"
+
+    sel = [at[r] for r in sorted(qrows)]
+    qr = torch.from_numpy(rows[sel]).to(dev)
+    check(f"dq ({len(sel)} rows)", out_to_f64(dq[qr[:, 0], qr[:, 1], qr[:, 2]]), rdq[sel])
+    got_kd, got_vd, ref_kd, ref_vd = [], [], [], []
+    for b, g, t in sorted(toks):
+        rs = [at[(b, g * G + j, t)] for j in range(G)]
+        ref_kd.append(sum(s * ds[r, t + 1:t + 1 + L, None] * qf[r] for r in rs))
+        ref_vd.append(sum(p[r, t + 1:t + 1 + L, None] * df[r] for r in rs))
+        got_kd.append(out_to_f64(dkd[b, g, t]))
+        got_vd.append(out_to_f64(dvd[b, g, t]))
+    check(f"dkd ({len(toks)} tokens)", np.stack(got_kd), np.stack(ref_kd))
+    check(f"dvd ({len(toks)} tokens)", np.stack(got_vd), np.stack(ref_vd))
+    ref_k, ref_v = [], []
+    for j in range(T - n_end, T):
+        rs = [at[(eb, eg * G + h, t)] for t in range(j, T) for h in range(G)]
+        ref_k.append(sum(s * ds[r, j] * qf[r] for r in rs))
+        ref_v.append(sum(p[r, j] * df[r] for r in rs))
+    check(f"dk (last {n_end} keys)", out_to_f64(dk[eb, eg, T - n_end:]), np.stack(ref_k))
+    check(f"dv (last {n_end} keys)", out_to_f64(dv[eb, eg, T - n_end:]), np.stack(ref_v))
+
+    # The identity over all keys, per (b, kv head) and dim, in fp64 on the
+    # device.  Each term carries independent round-to-nearest-even errors, so
+    # the sum's error is a random walk; the tolerance is 10 standard
+    # deviations, from root-sums-of-squares: each row's weights are rounded
+    # (2^-9 relative: their sum, 1, errs by at most 2^-9, times dO_t) and every
+    # stored dV, dVd by 2^-9.
+    f = lambda x: x.double()
+    rss = lambda x, dims: x.square().sum(dims).sqrt()
+    do_g = f(dout).view(B, Hkv, G, T, d)
+    gv, gvd = f(dv), f(dvd)
+    err_v = (gv.sum(2) + gvd.sum((2, 3)) - do_g.sum((2, 3))).abs()
+    sig_v = 2.0 ** -9 * (rss(do_g, (2, 3)) + rss(gv, 2) + rss(gvd, (2, 3)))
+    r_v = float((err_v / (10 * sig_v)).max())
+    # what the check would read if the depth entries' dV were missing
+    miss_v = float(((gv.sum(2) - do_g.sum((2, 3))).abs() / (10 * sig_v)).max())
+    print(f"[parity] bwd {cfg.get('name', '')} sum dV + sum dVd vs sum dO: error / 10 sigma "
+          f"{r_v:.3f} (without the depth terms: {miss_v:.1f})", flush=True)
+    assert r_v <= 1.0
+    del d_in, dout, dq, dk, dv, dkd, dvd
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["long_64k", "depth_heavy"])
+def test_bwd_full_size_sampled(m, dev, name):
+    """The backward at the 64K-token and depth-heavy workloads (sampled outputs
+    against the oracle's row-restricted backward, identities over all keys)."""
+    bwd_sampled_check(m, dict(WORKLOADS[name], name=name), dev)
+
+
 def test_bwd_layer_1p5b_full(m, dev):
     """B2 Hq16 Hkv4 T4096 d128 L24 (bf16 N(0,1)*0.5 inputs, N(0,1) dO): every
     element of every gradient against the oracle's backward."""
