@@ -474,9 +474,9 @@ def test_runs_on_nondefault_stream(m, dev):
 
 # ------------------------------------------------------------------ backward
 
-BWD_SHAPES = [  # (B, Hq, Hkv, T, L): G = 1, 2, 3, 4, 8; ragged T
+BWD_SHAPES = [  # (B, Hq, Hkv, T, L): G = 1, 2, 3, 4, 8, 32, 64; ragged T
     (1, 4, 4, 70, 0), (1, 8, 2, 130, 0), (2, 16, 4, 257, 0), (1, 8, 1, 100, 0), (1, 6, 2, 65, 0),
-    (1, 2, 2, 1, 0),
+    (1, 2, 2, 1, 0), (1, 64, 1, 150, 0),
     (1, 4, 4, 70, 5), (1, 8, 2, 130, 24), (1, 8, 1, 100, 33), (1, 6, 2, 65, 3), (2, 16, 4, 96, 1),
     (1, 32, 1, 40, 2), (1, 2, 2, 1, 7),
 ]
