@@ -239,9 +239,10 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
  *                      G query heads of each KV head)
  *   dk_depth, dv_depth: dKd, dVd [B, Hkv, T, L, d], written in full (NULL if L == 0)
  *   delta            : scratch [B, Hq, T] float32 that the call overwrites
- * Gradients are bf16 (fp32 accumulation).  Supports bf16 with d = 128 and
- * G = Hq / Hkv up to 64 (MODA_ERR_UNSUPPORTED otherwise).  Same validation,
- * ownership and asynchrony rules as moda_fwd. */
+ * Gradients are bf16 (fp32 accumulation).  Supports bf16 with d = 128,
+ * G = Hq / Hkv up to 64 (up to 32 when L > 0), G * T below 2^23 and T * L
+ * below 2^23 (MODA_ERR_UNSUPPORTED otherwise).  Same validation, ownership
+ * and asynchrony rules as moda_fwd. */
 moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const void *v,
                      const void *k_depth, const void *v_depth, const void *packed,
                      size_t packed_bytes, const void *out, const float *lse,
