@@ -18,6 +18,7 @@ HBM rates.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
+    python bench.py --sweep --sweep-bwd   # ... with the backward timed too
     python bench.py --decode-sweep     # one JSON line per decode shape
     python bench.py --stack --config layer_1p5b   # a stack of layers growing the depth stream
 
@@ -531,6 +532,8 @@ def main():
     ap.add_argument("--config", default="long_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-bwd", action="store_true",
+                    help="with --sweep: also time the backward at every point")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the group-unaware and masked-scan layout ablations (the "
                          "group-unaware one launches moda_fwd's kernel at other shapes)")
@@ -614,8 +617,8 @@ def main():
         for c in sweep_points():
             if args.only and args.only not in c["name"]:
                 continue
-            r = bench_config(c, args.steps, args.warmup, False, causal=True, with_bwd=False,
-                             ablation=args.ablation)
+            r = bench_config(c, args.steps, args.warmup, False, causal=True,
+                             with_bwd=args.sweep_bwd, ablation=args.ablation)
             print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
                               "pack_ms": r["pack_ms"], "causal_ms": r["causal_ms"],
@@ -632,7 +635,10 @@ def main():
                                                      if r["depth_ms"] else None),
                               "decode_us": r["decode_ms"] * 1e3 if r["decode_ms"] else None,
                               "decode_hbm_gbs": (decode_bytes(c) / r["decode_ms"] / 1e6
-                                                 if r["decode_ms"] else None)}), flush=True)
+                                                 if r["decode_ms"] else None),
+                              "bwd_ms": r["bwd_ms"],
+                              "bwd_tflops": (2.5 * flops(c) / r["bwd_ms"] / 1e9
+                                             if r["bwd_ms"] else None)}), flush=True)
         return
 
     cfg = dict(named[args.config])
