@@ -340,11 +340,28 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
   return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "depth launch");
 }
 
-moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const void *v,
-                     const void *k_depth, const void *v_depth, const void *packed,
-                     size_t packed_bytes, const void *out, const float *lse, const void *dout,
-                     void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth, float *delta,
-                     void *hip_stream) {
+namespace {
+
+// dK/dV split of the backward: when 128-key workgroups would not fill the chip
+// twice over, each key tile's query range goes to S parts (S <= 8, and at
+// least 4 query tiles per part of the heaviest key tile).
+int64_t bwd_splits(const moda_shape *s) {
+  const int64_t G = s->Hq / s->Hkv;
+  const int64_t base = (s->T + 127) / 128 * s->B * s->Hkv;
+  if (base >= 512) return 1;
+  int64_t S = (512 + base - 1) / base;
+  if (S > 8) S = 8;
+  const int64_t heaviest = (s->T + 64 / G - 1) / (64 / G);  // query tiles of key tile 0
+  if (S > heaviest / 4) S = heaviest / 4;
+  return S < 1 ? 1 : S;
+}
+
+size_t bwd_ws_bytes(const moda_shape *s) {
+  const int64_t S = bwd_splits(s);
+  return S > 1 ? (size_t)(2 * S * s->B * s->Hkv * s->T * s->d * 4) : 0;
+}
+
+moda_status bwd_check(const moda_shape *s) {
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (!use_mfma(s)) return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports bf16 with d = 128");
@@ -356,6 +373,18 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
       return fail(MODA_ERR_UNSUPPORTED, "moda_bwd with depth entries supports G up to 32");
     if (s->T * s->L >= ((int64_t)1 << 23))
       return fail(MODA_ERR_UNSUPPORTED, "moda_bwd supports T * L below 2^23");
+  }
+  return MODA_OK;
+}
+
+moda_status bwd_impl(const moda_shape *s, const void *q, const void *k, const void *v,
+                     const void *k_depth, const void *v_depth, const void *packed,
+                     size_t packed_bytes, const void *out, const float *lse, const void *dout,
+                     void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth, float *delta,
+                     int64_t nsplit, void *workspace, void *hip_stream) {
+  moda_status st = bwd_check(s);
+  if (st != MODA_OK) return st;
+  if (s->L > 0) {
     if (!k_depth || !v_depth || !dk_depth || !dv_depth)
       return fail(MODA_ERR_INVALID_ARG, "depth inputs and gradients must be non-NULL when L > 0");
     if (!aligned16(k_depth) || !aligned16(v_depth) || !aligned16(dk_depth) || !aligned16(dv_depth))
@@ -397,7 +426,43 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
   a.nblk = depth_blocks(s);
   a.scale = (float)(1.0 / std::sqrt((double)s->d));
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
+  a.nsplit = nsplit;
+  a.kv_ws = (float *)workspace;
   return hip_status(moda::launch_bwd(a, (hipStream_t)hip_stream), "bwd launch");
+}
+
+}  // namespace
+
+moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const void *v,
+                     const void *k_depth, const void *v_depth, const void *packed,
+                     size_t packed_bytes, const void *out, const float *lse, const void *dout,
+                     void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth, float *delta,
+                     void *hip_stream) {
+  return bwd_impl(s, q, k, v, k_depth, v_depth, packed, packed_bytes, out, lse, dout, dq, dk, dv,
+                  dk_depth, dv_depth, delta, 1, nullptr, hip_stream);
+}
+
+size_t moda_bwd_workspace_bytes(const moda_shape *s) {
+  if (!s || bwd_check(s) != MODA_OK) return 0;
+  return bwd_ws_bytes(s);
+}
+
+moda_status moda_bwd_ws(const moda_shape *s, const void *q, const void *k, const void *v,
+                        const void *k_depth, const void *v_depth, const void *packed,
+                        size_t packed_bytes, const void *out, const float *lse, const void *dout,
+                        void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth,
+                        float *delta, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+  moda_status st = bwd_check(s);
+  if (st != MODA_OK) return st;
+  const size_t need = bwd_ws_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MODA_ERR_INVALID_ARG, "workspace too small: need " + std::to_string(need) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+  if (need && (!workspace || !aligned16(workspace)))
+    return fail(MODA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  return bwd_impl(s, q, k, v, k_depth, v_depth, packed, packed_bytes, out, lse, dout, dq, dk, dv,
+                  dk_depth, dv_depth, delta, need ? bwd_splits(s) : 1, workspace, hip_stream);
 }
 
 moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k, const void *v,

@@ -345,9 +345,11 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
 
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
+  const int64_t S = p.nsplit;
   const int64_t x = blockIdx.x;
-  const int64_t ktile = x / BH;  // key tile 0 (the heaviest) first
-  const int64_t bh = x % BH;
+  const int64_t ktile = x / (BH * S);  // key tile 0 (the heaviest) first
+  const int64_t bh = (x % (BH * S)) / S;
+  const int64_t part = x % S;
   const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
   const int64_t k0 = ktile * KV_KEYS;
 
@@ -366,8 +368,12 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     for (int rr = 0; rr < 16; ++rr) acc[nb][rr] = 0.f;
 
   const float c = p.scale_log2;
-  // query tiles: tokens from k0 (the first that sees a key of this workgroup)
-  const int64_t n_qt = (T - k0 + TQr - 1) / TQr;
+  // query tiles: tokens from k0 (the first that sees a key of this workgroup);
+  // this workgroup takes part `part` of S even chunks of them
+  const int64_t n_all = (T - k0 + TQr - 1) / TQr;
+  const int64_t chunk = (n_all + S - 1) / S;
+  const int64_t qt_lo = part * chunk;
+  const int64_t n_qt = qt_lo + chunk < n_all ? qt_lo + chunk : n_all;  // one past the last
 
   // Tile loads.  Tile row r holds token t0 + r / G of head hkv*G + r % G; this
   // wave loads rows KV_ROWS*wave .. +KV_ROWS-1 of Q and of dO, each twice
@@ -432,9 +438,9 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     *(u32x4 *)(cg1 + o) = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  dma_tile(0, rq0, cq0, rg0, cg0);
-  {
-    const RowStats r0 = row_stats(0);
+  if (qt_lo < n_qt) {
+    dma_tile(qt_lo, rq0, cq0, rg0, cg0);
+    const RowStats r0 = row_stats(qt_lo);
     if (wave == 0) store_stats(0, r0);
   }
   wait_vmem();
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto run = [&](auto is_dk) __attribute__((always_inline)) {
-    int64_t qt = 0;
+    int64_t qt = qt_lo;
     for (; qt + 1 < n_qt; qt += 2) {
       body(qt, I0{}, is_dk);
       body(qt + 1, I1{}, is_dk);
@@ -557,9 +563,45 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   else
     run(std::false_type{});
 
-  if (key_ok)
+  if (!key_ok) return;
+  if (S == 1) {
     store_row((__bf16 *)(dk_wave ? p.dk : p.dv) + (bh * T + key) * BD, acc,
               dk_wave ? p.scale : 1.0f, lh);
+    return;
+  }
+  // this part's fp32 partial sums (zero if it had no query tile)
+  float *const ws =
+      p.kv_ws + (((dk_wave ? S : 0) + part) * BH * T + bh * T + key) * (int64_t)BD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(float4 *)(ws + 32 * nb + 8 * g + 4 * lh) =
+          float4{acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+}
+
+// Sum of the S parts' partial dV and dK (fp32) into the bf16 gradients; one
+// thread per 8 dims of a key.
+__global__ __launch_bounds__(256) void moda_bwd_kv_reduce(BwdArgs p) {
+  const int64_t BHT = p.B * p.Hkv * p.T;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (which * BHT + row) * 16 + c
+  if (i >= 2 * BHT * (BD / 8)) return;
+  const int64_t which = i / (BHT * (BD / 8));
+  const int64_t rc = i % (BHT * (BD / 8));
+  const int64_t S = p.nsplit;
+  const float *src = p.kv_ws + which * S * BHT * BD + rc * 8;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t sp = 0; sp < S; ++sp) {
+    const float4 lo = *(const float4 *)(src + sp * BHT * BD);
+    const float4 hi = *(const float4 *)(src + sp * BHT * BD + 4);
+    a[0] += lo.x; a[1] += lo.y; a[2] += lo.z; a[3] += lo.w;
+    a[4] += hi.x; a[5] += hi.y; a[6] += hi.z; a[7] += hi.w;
+  }
+  const float sc = which ? p.scale : 1.0f;
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = cvt_bf16x2(a[2 * q] * sc, a[2 * q + 1] * sc);
+  *(u32x4 *)((__bf16 *)(which ? p.dk : p.dv) + rc * 8) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -833,8 +875,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int64_t tq = DQ_ROWS / G;
   const int64_t dq_grid = (a.T + tq - 1) / tq * a.B * a.Hkv;
   hipLaunchKernelGGL(moda_bwd_dq, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
-  const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv;
+  const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv * a.nsplit;
   hipLaunchKernelGGL(moda_bwd_dkdv, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
+  if (a.nsplit > 1) {
+    const int64_t n = 2 * a.B * a.Hkv * a.T * (BD / 8);
+    hipLaunchKernelGGL(moda_bwd_kv_reduce, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, a);
+  }
   if (a.L > 0) {
     // after dq: it adds the depth entries' part to dQ
     const int64_t twg = (32 / G) * DD_SPANS;

@@ -46,6 +46,11 @@ struct BwdArgs {
   int64_t nblk;      // packed depth blocks per (b, kv head)
   float scale_log2;  // log2(e) / sqrt(d)
   float scale;       // 1 / sqrt(d)
+  // dK/dV split: each key tile's query range in nsplit parts; with nsplit > 1
+  // the parts leave fp32 partial sums in kv_ws [2][nsplit][B*Hkv][T][d]
+  // (dV, then unscaled dK), which a reduction kernel adds up
+  int64_t nsplit;
+  float *kv_ws;
 };
 
 // Decode step: one query row per (b, head) over a KV cache of T entries and

@@ -24,6 +24,7 @@ MODA_F32, MODA_BF16 = 0, 1
 # every symbol include/moda.h declares
 EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache", "moda_fwd",
            "moda_causal_fwd", "moda_depth_fwd", "moda_fwd_natural", "moda_bwd",
+           "moda_bwd_workspace_bytes", "moda_bwd_ws",
            "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
            "moda_fwd_layers", "moda_fwd_masked_scan", "moda_decode_varlen",
            "moda_fwd_strided",
@@ -65,6 +66,11 @@ def _load():
     lib.moda_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                              vp]
     lib.moda_bwd.restype = ctypes.c_int
+    lib.moda_bwd_workspace_bytes.argtypes = [sp]
+    lib.moda_bwd_workspace_bytes.restype = sz
+    lib.moda_bwd_ws.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, vp, sz, vp]
+    lib.moda_bwd_ws.restype = ctypes.c_int
     lib.moda_decode_workspace_bytes.argtypes = [sp]
     lib.moda_decode_workspace_bytes.restype = sz
     lib.moda_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -153,6 +159,18 @@ def moda_bwd(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_byte
     return lib.moda_bwd(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes,
                         out_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dkd_ptr, dvd_ptr,
                         delta_ptr, stream)
+
+
+def moda_bwd_workspace_bytes(shape: ModaShape) -> int:
+    return int(lib.moda_bwd_workspace_bytes(_sref(shape)))
+
+
+def moda_bwd_ws(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr, packed_bytes, out_ptr,
+                lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr, dkd_ptr, dvd_ptr, delta_ptr, ws_ptr,
+                ws_bytes, stream):
+    return lib.moda_bwd_ws(_sref(shape), q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, packed_ptr,
+                           packed_bytes, out_ptr, lse_ptr, dout_ptr, dq_ptr, dk_ptr, dv_ptr,
+                           dkd_ptr, dvd_ptr, delta_ptr, ws_ptr, ws_bytes, stream)
 
 
 def moda_decode_workspace_bytes(shape: ModaShape) -> int:
@@ -376,10 +394,14 @@ def fwd_layers(q, k, v, kl=None, vl=None, L=None, *, with_lse: bool = False, out
     return (out, lse) if with_lse else out
 
 
-def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, delta=None):
+def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, delta=None,
+        workspace=None, split: bool = True):
     """MoDA backward.  ``out`` and ``lse`` come from fwd(..., with_lse=True) on
     the same inputs.  Returns (dq, dk, dv, dkd, dvd); dkd, dvd are None when
-    L = 0.  ``grads`` may pass the five output tensors to fill."""
+    L = 0.  ``grads`` may pass the five output tensors to fill.  With ``split``
+    (moda_bwd_ws) a shape whose dK/dV work would not fill the GPU gets its
+    split, with ``workspace`` (a uint8 device tensor of at least
+    moda_bwd_workspace_bytes bytes) or one allocated here; without it, moda_bwd."""
     import torch
     _check_tensors(q, k, v, out, lse, dout, kd, vd, packed)
     B, Hq, T, d = q.shape
@@ -392,9 +414,19 @@ def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, d
         delta = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     nbytes = 0 if packed is None else packed.numel() * packed.element_size()
     dq, dk, dv, dkd, dvd = grads
-    _check(moda_bwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(packed), nbytes,
-                    _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
-                    _ptr(dvd), _ptr(delta), _stream_ptr(q)), "moda_bwd")
+    if not split:
+        _check(moda_bwd(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(packed),
+                        nbytes, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(dkd), _ptr(dvd), _ptr(delta), _stream_ptr(q)), "moda_bwd")
+        return grads
+    need = moda_bwd_workspace_bytes(shape)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(moda_bwd_ws(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _ptr(packed), nbytes,
+                       _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkd),
+                       _ptr(dvd), _ptr(delta), _ptr(workspace), ws_bytes, _stream_ptr(q)),
+           "moda_bwd_ws")
     return grads
 
 

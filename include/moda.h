@@ -249,6 +249,29 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
                      const void *dout, void *dq, void *dk, void *dv, void *dk_depth,
                      void *dv_depth, float *delta, void *hip_stream);
 
+/* Bytes of device workspace moda_bwd_ws uses for shape `s`: nonzero when the
+ * shape's dK/dV work would not fill the GPU (few KV heads times keys), in which
+ * case moda_bwd_ws splits each key range's query rows over several workgroups
+ * and adds their fp32 partial sums; 0 when no split pays, or when moda_bwd
+ * does not accept `s`.  Host only. */
+size_t moda_bwd_workspace_bytes(const moda_shape *s);
+
+/* The MoDA backward of moda_bwd (same passage, arguments, results, limits and
+ * rules), with a device workspace for its dK/dV split:
+ *   workspace : device scratch of workspace_bytes >= moda_bwd_workspace_bytes(s)
+ *               bytes (16-byte aligned; may be NULL when that is 0),
+ *               overwritten; its contents need no initialisation and mean
+ *               nothing after the call.  Two calls that overlap in time must
+ *               not share one workspace.
+ * A smaller workspace is MODA_ERR_INVALID_ARG.  The gradients equal moda_bwd's
+ * up to the order in which dK and dV sum their fp32 terms. */
+moda_status moda_bwd_ws(const moda_shape *s, const void *q, const void *k, const void *v,
+                        const void *k_depth, const void *v_depth, const void *packed,
+                        size_t packed_bytes, const void *out, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, void *dk_depth,
+                        void *dv_depth, float *delta, void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+
 /* Bytes of device workspace moda_decode needs for shape `s`; 0 if moda_decode
  * does not accept `s`.  Host only. */
 size_t moda_decode_workspace_bytes(const moda_shape *s);

@@ -146,6 +146,34 @@ def test_decode_workspace_and_rejects(m):
         m.MODA_ERR_INVALID_ARG
 
 
+def test_bwd_workspace_and_rejects(m):
+    """Backward: the dK/dV split's workspace is a host-side function of the
+    shape (0 where 128-key workgroups already fill the GPU twice over), and a
+    missing or short workspace comes back as a status before any device call."""
+    part = 4096 * 128 * 4  # one fp32 partial of one (b, kv head)'s dK or dV at T = 4096
+    # 32 key tiles x 4 KV heads = 128 workgroups: 4 parts
+    assert m.moda_bwd_workspace_bytes(shape(m, T=4096, L=24)) == 2 * 4 * 4 * part
+    # B = 2: 256 workgroups, 2 parts; two KV heads: 64, 8 parts
+    assert m.moda_bwd_workspace_bytes(shape(m, B=2, T=4096, L=24)) == 2 * 2 * 8 * part
+    assert m.moda_bwd_workspace_bytes(shape(m, Hkv=2, T=4096, L=0)) == 2 * 8 * 2 * part
+    # enough workgroups, or too few query tiles to split, or a shape moda_bwd refuses
+    assert m.moda_bwd_workspace_bytes(shape(m, T=65536, L=32)) == 0
+    assert m.moda_bwd_workspace_bytes(shape(m, T=70, L=5)) == 0
+    assert m.moda_bwd_workspace_bytes(shape(m, dtype="f32")) == 0
+    assert m.moda_bwd_workspace_bytes(shape(m, Hq=64, Hkv=1, L=24)) == 0
+    assert m.moda_bwd_workspace_bytes(None) == 0
+    s = shape(m, T=4096, L=24)
+    need = m.moda_bwd_workspace_bytes(s)
+    p = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    args = (p, p, p, p, p, p, 1 << 30, p, p, p, p, p, p, p, p, p)
+    assert m.moda_bwd_ws(s, *args, p, need - 1, None) == m.MODA_ERR_INVALID_ARG
+    assert "too small" in m.moda_last_error()
+    assert m.moda_bwd_ws(s, *args, None, need, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_bwd_ws(s, *args, mis, need, None) == m.MODA_ERR_INVALID_ARG
+    assert m.moda_bwd_ws(shape(m, dtype="f32"), *args, p, need, None) == m.MODA_ERR_UNSUPPORTED
+
+
 def test_append_rejects_before_launch(m):
     s = shape(m, T=100, L=24)
     p = ctypes.c_void_p(4096)

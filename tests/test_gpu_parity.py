@@ -483,7 +483,7 @@ BWD_SHAPES = [  # (B, Hq, Hkv, T, L): G = 1, 2, 3, 4, 8, 32, 64; ragged T
 BWD_TOL = 2e-2  # max-abs error relative to max(1, max |reference|) of each gradient
 
 
-def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
+def bwd_check(m, dev, B, Hq, Hkv, T, L, seed, split=True):
     from synth import f32_to_bf16_bits
     from gpu_util import to_dev
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=seed)
@@ -494,7 +494,7 @@ def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
     kd, vd = (d_in["kd"], d_in["vd"]) if L else (None, None)
     packed = m.pack_depth_cache(kd, vd, m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) if L else None
     out, lse = m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
-    grads = m.bwd(d_in["q"], d_in["k"], d_in["v"], out, lse, d_do, kd, vd, packed)
+    grads = m.bwd(d_in["q"], d_in["k"], d_in["v"], out, lse, d_do, kd, vd, packed, split=split)
     torch.cuda.synchronize()
     ref = oracle.moda_backward(h_in["q"], h_in["k"], h_in["v"], h_in["kd"] if L else None,
                                h_in["vd"] if L else None, h_do)
@@ -506,6 +506,7 @@ def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
         print(f"[parity] bwd {B,Hq,Hkv,T,L} {name} max|err|={e:.3e} max|ref|={scale:.3e}",
               flush=True)
         assert e <= BWD_TOL * scale, f"{name}: {e} > {BWD_TOL} * {scale}"
+    return grads
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", BWD_SHAPES,
@@ -513,6 +514,31 @@ def bwd_check(m, dev, B, Hq, Hkv, T, L, seed):
 def test_bwd_parity(m, dev, B, Hq, Hkv, T, L):
     """moda_bwd against the oracle's backward, every element of every gradient."""
     bwd_check(m, dev, B, Hq, Hkv, T, L, seed=300 + T + 7 * Hq)
+
+
+SPLIT_SHAPES = [(2, 16, 4, 257, 0), (1, 8, 2, 130, 24), (1, 16, 2, 700, 8)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", SPLIT_SHAPES,
+                         ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in SPLIT_SHAPES])
+def test_bwd_split_and_unsplit(m, dev, B, Hq, Hkv, T, L):
+    """Shapes whose dK/dV work moda_bwd_ws splits over several workgroups: the
+    unsplit moda_bwd against the oracle too, and the two within two bf16 ulps
+    of each other, floored at 2^-12 of the gradient's largest entry (they differ
+    only in the order fp32 terms are summed)."""
+    shape = m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")
+    assert m.moda_bwd_workspace_bytes(shape) > 0
+    seed = 300 + T + 7 * Hq
+    g_split = bwd_check(m, dev, B, Hq, Hkv, T, L, seed, split=True)
+    g_plain = bwd_check(m, dev, B, Hq, Hkv, T, L, seed, split=False)
+    for name, a, b in zip(("dq", "dk", "dv", "dkd", "dvd"), g_split, g_plain):
+        if a is None:
+            continue
+        a, b = out_to_f64(a), out_to_f64(b)
+        # two bf16 ulps, with a floor for entries near zero (where summation
+        # order moves the result by much more than its own ulp)
+        bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 2.0 ** -12 * np.max(np.abs(a))
+        assert np.all(np.abs(a - b) <= bound), f"{name}: split and unsplit differ"
 
 
 def bwd_sampled_check(m, cfg, dev, n_rows=16, n_tokens=4, n_end=3):
