@@ -311,6 +311,10 @@ constexpr int QROWS = 64;
 constexpr int KV_ROWS = QROWS / KV_WAVES;  // query tile rows each wave loads
 constexpr int KV_DMA = KV_ROWS / 4;        // 4-row load instructions per copy
 
+// SPLIT: the query range of each key tile is cut into p.nsplit parts, one per
+// workgroup, that leave fp32 partial sums (moda_bwd_kv_reduce adds them up);
+// without it, one part that stores the bf16 gradients itself.
+template <bool SPLIT>
 __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQr = QROWS / G;  // tokens per query tile (G <= 64)
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
 
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
-  const int64_t S = p.nsplit;
+  const int64_t S = SPLIT ? p.nsplit : 1;
   const int64_t x = blockIdx.x;
   const int64_t ktile = x / (BH * S);  // key tile 0 (the heaviest) first
   const int64_t bh = (x % (BH * S)) / S;
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     run(std::false_type{});
 
   if (!key_ok) return;
-  if (S == 1) {
+  if constexpr (!SPLIT) {
     store_row((__bf16 *)(dk_wave ? p.dk : p.dv) + (bh * T + key) * BD, acc,
               dk_wave ? p.scale : 1.0f, lh);
     return;
@@ -876,7 +880,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int64_t dq_grid = (a.T + tq - 1) / tq * a.B * a.Hkv;
   hipLaunchKernelGGL(moda_bwd_dq, dim3((uint32_t)dq_grid), dim3(64 * DQ_WAVES), 0, s, a);
   const int64_t kv_grid = (a.T + KV_KEYS - 1) / KV_KEYS * a.B * a.Hkv * a.nsplit;
-  hipLaunchKernelGGL(moda_bwd_dkdv, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL(moda_bwd_dkdv<true>, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL(moda_bwd_dkdv<false>, dim3((uint32_t)kv_grid), dim3(64 * KV_WAVES), 0, s,
+                       a);
   if (a.nsplit > 1) {
     const int64_t n = 2 * a.B * a.Hkv * a.T * (BD / 8);
     hipLaunchKernelGGL(moda_bwd_kv_reduce, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, a);
