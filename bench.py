@@ -463,14 +463,16 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                  torch.empty_like(kd) if L else None, torch.empty_like(vd) if L else None)
         delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ws_n = moda.moda_bwd_workspace_bytes(shape)
+        bwd_ws = torch.empty((ws_n,), dtype=torch.uint8, device=dev) if ws_n else None
 
         def bwd():
             moda.bwd(q, k, v, o_b, lse_b, dout, kd if L else None, vd if L else None, packed,
-                     grads=grads, delta=delta)
+                     grads=grads, delta=delta, workspace=bwd_ws)
 
         bwd()
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
-        del o_b, lse_b, dout, grads, delta
+        del o_b, lse_b, dout, grads, delta, bwd_ws
     res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
                append_ms=append_ms, append2_ms=append2_ms, layers_ms=layers_ms,
