@@ -612,16 +612,16 @@ __global__ __launch_bounds__(256) void moda_bwd_kv_reduce(BwdArgs p) {
 // Depth gradients: dKd, dVd and the depth entries' part of dQ.  A workgroup
 // covers DD_SPANS spans of TW = floor(32/G) whole tokens (their G query rows
 // each, 32 rows at most), with two waves per span on one SIMD:
-//   the entry wave (a lane per entry of a 32-entry block): S_d = Q Kd^T, P_d,
-//     dP_d = dO Vd^T, dS_d; dVd^T = dO^T P_d and dKd^T = Q^T dS_d, with Q^T
-//     and dO^T read transposed from the span's rows stored once in LDS;
-//   the row wave (a lane per query row): S_d^T = Kd Q^T, P_d^T,
-//     dP_d^T = Vd dO^T, dS_d^T; dQ^T += Kd^T dS_d^T, with Kd^T read
-//     transposed from the block's K rows, which the wave copies from its
-//     registers into LDS; at the end it adds the sum to dQ, which holds the
-//     sequence part.
-// Both waves read the same blocks (packed K half, natural Vd rows) at about
-// the same time, so the second read is served by L2.  Every row that reads
+//   the entry wave (a lane per entry of a 32-entry block) reads the block
+//     (packed K half, natural Vd rows) once and computes S_d = Q Kd^T, P_d,
+//     dP_d = dO Vd^T and dS_d; it passes the block's K rows and dS_d to the
+//     row wave through LDS, then forms dVd^T = dO^T P_d and dKd^T = Q^T dS_d,
+//     with Q^T and dO^T read transposed from the span's rows stored once in
+//     LDS; the next block's loads are in flight meanwhile;
+//   the row wave (a lane per query row) accumulates dQ^T += Kd^T dS_d^T from
+//     the two hand-over buffers and at the end adds the sum to dQ, which holds
+//     the sequence part.
+// Two workgroup barriers per block order the hand-over.  Every row that reads
 // an entry is in the entry's span, so no atomics are needed.
 // ---------------------------------------------------------------------------
 constexpr int DD_SPANS = 4;
@@ -635,6 +635,7 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char g_s[DD_SPANS][32 * 256];
   __shared__ __attribute__((aligned(1024))) char k_s[DD_SPANS][32 * 256];
   __shared__ __attribute__((aligned(1024))) char o_s[DD_SPANS][32 * 256];  // output staging
+  __shared__ __attribute__((aligned(1024))) char x_s[DD_SPANS][32 * 64];   // dS_d^T, bf16
   __shared__ __attribute__((aligned(16))) float lse_s[DD_SPANS][32];  // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float del_s[DD_SPANS][32];  // -D
 
@@ -652,24 +653,39 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
   const int64_t x = blockIdx.x;
   const int64_t bh = x % BH;
   const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
-  const int64_t wt_lo = (x / BH) * TWG + (int64_t)span * TW;  // the span's first token
-  int64_t wt_hi = wt_lo + TW;
-  if (wt_hi > T) wt_hi = T;
+  const int64_t wg_lo = (x / BH) * TWG;
+  // blocks holding entries of the span starting at token lo (0 past the end)
+  auto span_blocks = [&](int64_t lo) -> int64_t {
+    if (lo >= T) return 0;
+    const int64_t hi = lo + TW < T ? lo + TW : T;
+    return (hi * L + kDepthBlock - 1) / kDepthBlock - lo * L / kDepthBlock;
+  };
+  // every wave walks the workgroup's longest span so that all meet at each barrier
+  int64_t n_iter = 0;
+  for (int s = 0; s < DD_SPANS; ++s) {
+    const int64_t n = span_blocks(wg_lo + (int64_t)s * TW);
+    n_iter = n > n_iter ? n : n_iter;
+  }
+  const int64_t wt_lo = wg_lo + (int64_t)span * TW;  // the span's first token
+  const int64_t wt_hi = wt_lo + TW < T ? wt_lo + TW : T;
+  const int64_t e_lo = wt_lo * L, e_hi = wt_hi * L;  // entries of the span's tokens
+  const int64_t blk_lo = e_lo / kDepthBlock;
+  const int64_t blk_hi = blk_lo + span_blocks(wt_lo);
 
-  // this lane's row: an MFMA operand of either wave, and the LDS copies
+  // this lane's row: the entry wave's copy into LDS, the row wave's dQ row
   const int r = li;
   const bool row_used = r < TW * G;
   const int64_t tok = wt_lo + r / G;
   const bool row_ok = row_used && tok < T;
   const int64_t head = hkv * G + (row_used ? r % G : 0);
   const int64_t qrow = (b * p.Hq + head) * T + (row_ok ? tok : 0);
-  bf16x8 qb[8], gb[8];
-  load_row_operand((const __bf16 *)p.q + qrow * BD, row_ok, lh, qb);
-  load_row_operand((const __bf16 *)p.dout + qrow * BD, row_ok, lh, gb);
-  // rows outside the problem get weight 0
-  const float l_row = row_ok ? -LOG2E * p.lse[qrow] : -INFINITY;
-  const float d_row = row_ok ? -p.delta[qrow] : 0.f;
   if (!row_wave) {
+    bf16x8 qb[8], gb[8];
+    load_row_operand((const __bf16 *)p.q + qrow * BD, row_ok, lh, qb);
+    load_row_operand((const __bf16 *)p.dout + qrow * BD, row_ok, lh, gb);
+    // rows outside the problem get weight 0
+    const float l_row = row_ok ? -LOG2E * p.lse[qrow] : -INFINITY;
+    const float d_row = row_ok ? -p.delta[qrow] : 0.f;
     char *const qs = q_s[span];
     char *const gs = g_s[span];
 #pragma unroll
@@ -683,45 +699,68 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
       del_s[span][r] = d_row;
     }
   }
-  __syncthreads();
-  if (wt_lo >= T) return;
 
   const float c = p.scale_log2;
-  const int64_t e_lo = wt_lo * L, e_hi = wt_hi * L;  // entries of the span's tokens
-  const int64_t blk_lo = e_lo / kDepthBlock;
-  const int64_t blk_hi = (e_hi + kDepthBlock - 1) / kDepthBlock;
-  const char *const pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
-  const __bf16 *const vnat = (const __bf16 *)p.vd + bh * TL * BD;
-  // the block's Kd rows (packed K half: lane = entry, 8 dims a k-step) and Vd
-  // rows (natural) as MFMA operands; the sixteen loads go out together
-  auto load_block = [&](int64_t blk, u32x4 (&kd)[8], u32x4 (&vr)[8]) {
-    const int64_t e = blk * kDepthBlock + li;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kd[ks] = *(const u32x4 *)(pk + blk * kPackedBlockBytes + ks * 1024);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      vr[ks] = e < TL ? *(const u32x4 *)(vnat + e * BD + 64 * lh + 8 * ks) : u32x4{0, 0, 0, 0};
-  };
+  char *const ks_ = k_s[span];
+  char *const xs = x_s[span];
+  // the row wave's B operand: dS_d^T read transposed from x_s (rows of 64
+  // bytes, no swizzle), the same lane pattern as TileFrags::colfrag
+  const int lg = lane >> 4, lq = lane & 15;
+  const int xaddr = (4 * (lg >> 1) + (lq >> 2)) * 64 + 16 * (2 * (lg & 1) + ((lq & 3) >> 1)) +
+                    8 * (lq & 1);
 
+  // Per block: the entry wave (a lane per entry) computes S_d = Q Kd^T,
+  // dP_d = dO Vd^T, P_d and dS_d, hands the K rows and dS_d to the row wave
+  // through LDS, then forms dVd and dKd; the row wave (a lane per query row)
+  // accumulates dQ^T += Kd^T dS_d^T.  The depth block is read from memory once.
+  // Both kinds of wave pass the same barriers, n_iter times each: one before
+  // the hand-over buffers are rewritten, one after they are filled.
   if (!row_wave) {
-    const char *const qs = q_s[span];
-    const char *const gs = g_s[span];
-    for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+    // Every load and store of the loop is a buffer instruction over the
+    // block's own range, so none is skipped: entries past the stream and
+    // blocks past the span read zeros, and rows the span does not own are
+    // dropped.  The loads of the next block then stay counted ahead of this
+    // block's stores, and the wait for them never waits for the stores.
+    const char *const pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes;
+    const char *const vnat = (const char *)p.vd + bh * TL * (BD * 2);
+    auto load_block = [&](int64_t blk, u32x4(&kd)[8], u32x4(&vr)[8])
+                          __attribute__((always_inline)) {
+      const bool in = blk < blk_hi;
+      const int64_t left = TL - blk * kDepthBlock;
+      const int vrows = !in ? 0 : left < kDepthBlock ? (int)left : kDepthBlock;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(pk + blk * kPackedBlockBytes), (short)0, in ? (int)kPackedBlockBytes : 0,
+          0x00020000);
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(vnat + blk * kDepthBlock * (BD * 2)), (short)0, vrows * (BD * 2), 0x00020000);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kd[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane * 16 + ks * 1024, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        vr[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, li * 256 + 128 * lh + 16 * ks, 0, 0);
+    };
+    // S_d = Q Kd^T and dP_d = dO Vd^T (rows x entries), then P_d and
+    // dS_d = P_d (dP_d - D) as bf16 B operands
+    auto scores = [&](int64_t blk, const u32x4(&kd)[8], const u32x4(&vr)[8], bf16x8(&pb)[2],
+                      bf16x8(&dsb)[2]) __attribute__((always_inline)) {
       const int64_t e = blk * kDepthBlock + li;  // this lane's entry
-      u32x4 kd[8], vr[8];
-      load_block(blk, kd, vr);
-      __builtin_amdgcn_sched_barrier(0);
-      // S_d = Q Kd^T and dP_d = dO Vd^T (rows x entries)
       floatx16 sd, dpd;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) sd[rr] = dpd[rr] = 0.f;
+      // the row operands come from their LDS copies (registers are kept for
+      // the next block's loads); the opaque offset keeps them in the loop
+      int roff = r * 256;
+      asm volatile("" : "+v"(roff));
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[ks], __builtin_bit_cast(bf16x8, kd[ks]),
-                                                     sd, 0, 0, 0);
-        dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[ks], __builtin_bit_cast(bf16x8, vr[ks]),
-                                                      dpd, 0, 0, 0);
+        const int off = roff + 16 * col_swz(r, 8 * lh + ks);
+        sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(q_s[span] + off),
+                                                     __builtin_bit_cast(bf16x8, kd[ks]), sd, 0, 0,
+                                                     0);
+        dpd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(g_s[span] + off),
+                                                      __builtin_bit_cast(bf16x8, vr[ks]), dpd, 0,
+                                                      0, 0);
       }
       // register rr holds row 8*(rr/4) + 4*lh + rr%4: keep it iff the row is
       // one of the G rows of the entry's token, i.e. row - etok*G in [0, G)
@@ -730,8 +769,6 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr)
         if ((unsigned)(8 * (rr >> 2) + (rr & 3) + base) >= (unsigned)G) sd[rr] = -INFINITY;
-      // P_d and dS_d = P_d (dP_d - D) as bf16 B operands
-      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const float4 la = *(const float4 *)&lse_s[span][8 * (2 * kk) + 4 * lh];
@@ -752,11 +789,41 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
         pb[kk] = __builtin_bit_cast(bf16x8, w);
         dsb[kk] = __builtin_bit_cast(bf16x8, wd);
       }
+    };
+
+    u32x4 kd[8], vr[8];
+    bf16x8 pb[2], dsb[2];
+    load_block(blk_lo, kd, vr);
+    __syncthreads();  // the span's rows and statistics are in LDS
+    scores(blk_lo, kd, vr, pb, dsb);
+    for (int64_t it = 0; it < n_iter; ++it) {
+      const int64_t blk = blk_lo + it;
+      __syncthreads();  // the row waves are done with the previous block's K rows and dS_d
+      // K rows column-swizzled; dS_d^T as [entry][row]: dsb[kk] holds rows
+      // 16kk + 4lh + 0..3 and 16kk + 8 + 4lh + 0..3 of entry li
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        *(u32x4 *)(ks_ + li * 256 + 16 * col_swz(li, 8 * lh + ks)) = kd[ks];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 w = __builtin_bit_cast(u32x4, dsb[kk]);
+        *(u32x2 *)(xs + li * 64 + 32 * kk + 8 * lh) = u32x2{w[0], w[1]};
+        *(u32x2 *)(xs + li * 64 + 32 * kk + 16 + 8 * lh) = u32x2{w[2], w[3]};
+      }
+      // the next block's loads land while this one's gradients are formed
+      load_block(blk + 1, kd, vr);
+      __syncthreads();  // K rows and dS_d of this block are in LDS
       // dVd^T = dO^T P_d, then dKd^T = Q^T dS_d (the span's 32 rows as two
       // k-steps), one accumulator set at a time.  Each goes to LDS as the
       // block's 32 rows (chunk c of row r in slot c ^ (r % 16)) and from there
-      // to memory four whole rows per instruction.
+      // to memory four whole rows per instruction, rows the span owns only.
+      const char *const qs = q_s[span];
+      const char *const gs = g_s[span];
       char *const os = o_s[span];
+      const int64_t b0 = blk * kDepthBlock;
+      const int lo_r = e_lo > b0 ? (int)(e_lo - b0) : 0;
+      const int hi_r = e_hi - b0 < kDepthBlock ? (int)(e_hi - b0) : kDepthBlock;
+      const int nrec = hi_r > 0 ? hi_r * (BD * 2) : 0;
 #pragma unroll
       for (int which = 0; which < 2; ++which) {
         floatx16 acc[4];
@@ -781,77 +848,48 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
             o[1] = cvt_bf16x2(acc[nb][4 * g + 2] * sc, acc[nb][4 * g + 3] * sc);
             *(u32x2 *)(os + li * 256 + 16 * ((4 * nb + g) ^ (li & 15)) + 8 * lh) = o;
           }
-        __bf16 *const dst = (__bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + blk * kDepthBlock) * BD;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((const __bf16 *)(which ? p.dkd : p.dvd) + (bh * TL + b0) * BD), (short)0,
+            nrec, 0x00020000);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int rr = 4 * i + (lane >> 4), cc = lane & 15;
           const u32x4 v = *(const u32x4 *)(os + rr * 256 + 16 * (cc ^ (rr & 15)));
-          const int64_t er = blk * kDepthBlock + rr;
-          if (er >= e_lo && er < e_hi) *(u32x4 *)(dst + rr * BD + 8 * cc) = v;
+          const int voff = rr >= lo_r ? rr * (BD * 2) + 16 * cc : (int)0x80000000;
+          __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, voff, 0, 0);
         }
       }
+      // the next block's scores (past the span: unused)
+      scores(blk + 1, kd, vr, pb, dsb);
     }
     return;
   }
 
   // row wave
-  char *const ks_ = k_s[span];
   floatx16 dq[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) dq[nb][rr] = 0.f;
-  const int64_t my_lo = tok * L;  // this row's token's first entry
-  for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
-    u32x4 kd[8], vr[8];
-    load_block(blk, kd, vr);
-    __builtin_amdgcn_sched_barrier(0);
-    // the block's K rows into LDS, column-swizzled, for the transposed product
-    // (LDS operations of one wave run in order: the last block's reads are done)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      *(u32x4 *)(ks_ + li * 256 + 16 * col_swz(li, 8 * lh + ks)) = kd[ks];
-    // S_d^T = Kd Q^T and dP_d^T = Vd dO^T (entries x rows)
-    floatx16 st, dpt;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) st[rr] = dpt[rr] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kd[ks]), qb[ks], st,
-                                                   0, 0, 0);
-      dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vr[ks]), gb[ks],
-                                                    dpt, 0, 0, 0);
-    }
-    // register rr holds entry blk*32 + 8*(rr/4) + 4*lh + rr%4: keep it iff it
-    // is one of this row's token's entries
-    {
-      const int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
-      const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) st[rr] = -INFINITY;
-    }
-    // dS_d^T = P_d^T (dP_d^T - D) as bf16 B operands
-    bf16x8 dsb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 w;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = 8 * kk + 2 * q;
-        const float p0 = fast_exp2(fmaf(c, st[rr], l_row));
-        const float p1 = fast_exp2(fmaf(c, st[rr + 1], l_row));
-        w[q] = cvt_bf16x2(p0 * (dpt[rr] + d_row), p1 * (dpt[rr + 1] + d_row));
-      }
-      dsb[kk] = __builtin_bit_cast(bf16x8, w);
-    }
+  __syncthreads();
+  for (int64_t it = 0; it < n_iter; ++it) {
+    __syncthreads();
+    __syncthreads();
+    if (blk_lo + it >= blk_hi) continue;
     // dQ^T += Kd^T dS_d^T over the block's 32 entries (two k-steps)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
+      const char *const vp = xs + xaddr + kk * 16 * 64;
+      const shortx4 lo = lds_read_tr(vp);
+      const shortx4 hi = lds_read_tr(vp + 8 * 64);
+      const bf16x8 xb = __builtin_bit_cast(
+          bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(ks_, 4 * nb + kk), dsb[kk],
+        dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(ks_, 4 * nb + kk), xb,
                                                          dq[nb], 0, 0, 0);
+    }
   }
   // dQ (the sequence part, as written) += s * the depth part
   if (row_ok) {
