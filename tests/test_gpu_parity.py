@@ -646,6 +646,16 @@ def test_bwd_full_size_sampled(m, dev, name):
     bwd_sampled_check(m, dict(WORKLOADS[name], name=name), dev)
 
 
+def test_bwd_near_size_limit_sampled(m, dev):
+    """The backward with T*L just under its 2^23 limit (T = 65536, L = 127,
+    G = 4): every flat depth-entry offset and per-head extent at its largest,
+    sampled against the oracle as above."""
+    cfg = dict(B=1, Hq=4, Hkv=1, T=65536, L=127, d=128, dtype="bf16", scale=1.0, seed=6000,
+               name="T65536_L127")
+    assert cfg["T"] * cfg["L"] < 1 << 23
+    bwd_sampled_check(m, cfg, dev)
+
+
 def test_bwd_layer_1p5b_full(m, dev):
     """B2 Hq16 Hkv4 T4096 d128 L24 (bf16 N(0,1)*0.5 inputs, N(0,1) dO): every
     element of every gradient against the oracle's backward."""
