@@ -209,6 +209,36 @@ def test_fwd_layers_matches_packed(m, dev, B, Hq, Hkv, T, L):
     assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
 
 
+def test_fwd_near_size_limit(m, dev):
+    """T*L just under its 2^23 limit (T = 65536, L = 127, G = 4): the packed
+    forward against the oracle on sampled rows, and the natural-layout and
+    layer-major forwards, whose depth reads span all T*L rows, equal to it bit
+    for bit."""
+    cfg = dict(B=1, Hq=4, Hkv=1, T=65536, L=127, d=128, dtype="bf16", scale=1.0, seed=6100,
+               name="T65536_L127")
+    assert cfg["T"] * cfg["L"] < 1 << 23
+    d_in = device_case(cfg, dev)
+    out, lse = run_full(m, d_in, cfg["L"])
+    rows = sample_rows(cfg, n_random=64, seed=cfg["seed"])
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
+    e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
+    print(f"[parity] {cfg['name']} rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}",
+          flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                                 with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
+    del out_n, lse_n
+    out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], layer_major(d_in["kd"]),
+                                layer_major(d_in["vd"]), with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
+    del d_in, out, lse, out_l, lse_l
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
                          ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
 def test_fwd_masked_scan_matches_natural(m, dev, B, Hq, Hkv, T, L):
