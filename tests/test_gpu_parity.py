@@ -925,6 +925,28 @@ def test_append_builds_the_cache(m, dev, B, Hkv, T, L, groups):
     assert torch.equal(cache, ref)
 
 
+def test_append_near_size_limit(m, dev):
+    """T*L just under its 2^23 limit (T = 65536, L = 127): writing the last
+    entry of every token into a cache packed without it gives the repack of
+    the whole stream byte for byte (compared on the device)."""
+    B, Hkv, T, L = 1, 1, 65536, 127
+    cfg = dict(B=B, Hq=4, Hkv=Hkv, T=T, L=L, d=128, dtype="bf16", scale=1.0, seed=6200)
+    d_in = device_case(cfg, dev)
+    shape = m.make_shape(B, 4, Hkv, T, L, 128, "bf16")
+    kd0, vd0 = d_in["kd"].clone(), d_in["vd"].clone()
+    kd0[:, :, :, L - 1] = 0
+    vd0[:, :, :, L - 1] = 0
+    cache = m.pack_depth_cache(kd0, vd0, shape)
+    del kd0, vd0
+    m.append_depth(cache, shape, L - 1, d_in["kd"][:, :, :, L - 1:].contiguous(),
+                   d_in["vd"][:, :, :, L - 1:].contiguous())
+    ref = m.pack_depth_cache(d_in["kd"], d_in["vd"], shape)
+    torch.cuda.synchronize()
+    assert torch.equal(cache, ref)
+    del d_in, cache, ref
+    torch.cuda.empty_cache()
+
+
 def test_append_replaces_one_entry(m, dev):
     """Writing entry i over a packed cache changes exactly entry i of every
     token: the forward on it equals the forward on a fresh repack of the
