@@ -181,7 +181,11 @@ def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
     dt, work, n = run(nrows)
     tflops = work / dt / 1e12
     full_s = flops(cfg) / (work / dt)
-    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    # cores: the host CPUs this process may run on; threads: the OpenMP threads the
+    # oracle ran with (OMP_NUM_THREADS, else one per core)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores,
+            "threads": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} random (b,h,t) rows of the same workload, fp64, {dt:.1f} s; "
                       f"full workload extrapolated to {full_s:.0f} s"}
 

@@ -245,9 +245,49 @@ def _check_tensors(*ts):
             raise ValueError("libmoda takes contiguous tensors")
 
 
+def _expect(name, t, shape, dtype=None, device=None):
+    """Raise ValueError unless tensor t has exactly this shape (and dtype and
+    device, when given).  The C ABI receives bare pointers and cannot check
+    these itself: a short or mistyped tensor would be read past its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_qkv(q, k, v):
+    """q [B,Hq,T,d]; k, v [B,Hkv,T,d] of q's dtype and device.  Returns B, Hq, Hkv, T, d."""
+    if q is None or k is None or v is None:
+        raise ValueError("q, k and v are required")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D: [B,Hq,T,d] and [B,Hkv,T,d]")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    _expect("k", k, (B, Hkv, T, d), q.dtype, q.device)
+    _expect("v", v, (B, Hkv, T, d), q.dtype, q.device)
+    return B, Hq, Hkv, T, d
+
+
+def _check_out(q, out, lse, lse_shape):
+    if out is not None:
+        _expect("out", out, q.shape, q.dtype, q.device)
+    if lse is not None:
+        import torch
+        _expect("lse", lse, lse_shape, torch.float32, q.device)
+
+
 def pack_depth_cache(kd, vd, shape: ModaShape | None = None, out=None):
     """Repack Kd, Vd [B,Hkv,T,L,d] into a new (or given) uint8 device buffer."""
     import torch
+    if kd is None or kd.dim() != 5:
+        raise ValueError("kd must be 5-D: [B,Hkv,T,L,d]")
+    _expect("vd", vd, kd.shape, kd.dtype, kd.device)
+    if shape is not None:
+        _expect("kd", kd, (shape.B, shape.Hkv, shape.T, shape.L, shape.d))
     _check_tensors(kd, vd)
     if shape is None:
         B, Hkv, T, L, d = kd.shape
@@ -264,9 +304,12 @@ def fwd(q, k, v, packed=None, L: int = 0, *, with_lse: bool = False, out=None, l
     """MoDA forward.  ``packed`` comes from pack_depth_cache with the same
     shape (the Hq of the pack shape does not matter; only B, Hkv, T, L, d)."""
     import torch
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
+    _check_out(q, out, lse, (B, Hq, T))
+    if packed is not None and packed.device != q.device:
+        raise ValueError("packed must be on q's device")
     _check_tensors(q, k, v, packed)
-    B, Hq, T, d = q.shape
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -280,9 +323,10 @@ def fwd(q, k, v, packed=None, L: int = 0, *, with_lse: bool = False, out=None, l
 def causal_fwd(q, k, v, *, with_lse: bool = False, out=None, lse=None):
     """Causal-only attention (the same kernel without the depth part)."""
     import torch
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
+    _check_out(q, out, lse, (B, Hq, T))
     _check_tensors(q, k, v)
-    B, Hq, T, d = q.shape
-    shape = make_shape(B, Hq, k.shape[1], T, 0, d, q.dtype)
+    shape = make_shape(B, Hq, Hkv, T, 0, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -296,8 +340,11 @@ def depth_fwd(q, packed, Hkv: int, L: int, *, with_lse: bool = False, out=None, 
     """Depth attention alone over a packed depth cache (the same packed
     buffer moda_fwd reads; Hkv and L are those of the pack shape)."""
     import torch
-    _check_tensors(q, packed)
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be 4-D: [B,Hq,T,d]")
     B, Hq, T, d = q.shape
+    _check_out(q, out, lse, (B, Hq, T))
+    _check_tensors(q, packed)
     shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
@@ -321,10 +368,14 @@ def depth_forward(q, kd, vd, *, with_lse: bool = False):
 def fwd_natural(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=None):
     """MoDA forward straight from the natural depth layout (no repack)."""
     import torch
-    _check_tensors(q, k, v, kd, vd)
-    B, Hq, T, d = q.shape
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
     L = 0 if kd is None else kd.shape[3]
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if kd is not None:
+        _expect("kd", kd, (B, Hkv, T, L, d), q.dtype, q.device)
+        _expect("vd", vd, (B, Hkv, T, L, d), q.dtype, q.device)
+    _check_out(q, out, lse, (B, Hq, T))
+    _check_tensors(q, k, v, kd, vd)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -339,9 +390,15 @@ def fwd_masked_scan(q, k, v, kd, vd, *, with_lse: bool = False, out=None, lse=No
     """Layout ablation: moda_fwd_natural's result, with every query tile
     scanning the flattened depth axis from entry 0 under the own-token mask."""
     import torch
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
+    if kd is None or kd.dim() != 5:
+        raise ValueError("kd must be 5-D: [B,Hkv,T,L,d]")
+    L = kd.shape[3]
+    _expect("kd", kd, (B, Hkv, T, L, d), q.dtype, q.device)
+    _expect("vd", vd, (B, Hkv, T, L, d), q.dtype, q.device)
+    _check_out(q, out, lse, (B, Hq, T))
     _check_tensors(q, k, v, kd, vd)
-    B, Hq, T, d = q.shape
-    shape = make_shape(B, Hq, k.shape[1], T, kd.shape[3], d, q.dtype)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -357,11 +414,17 @@ def fwd_capacity(q, k, v, kd=None, vd=None, L=None, *, with_lse: bool = False, o
     entries: kd, vd [B,Hkv,T,Lcap,d], of which the first L (default: all) are
     the depth entries (moda_fwd_strided with strides (T*Lcap, Lcap, 1))."""
     import torch
-    _check_tensors(q, k, v, kd, vd)
-    B, Hq, T, d = q.shape
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
     Lcap = 0 if kd is None else kd.shape[3]
     L = Lcap if L is None else L
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if kd is not None:
+        _expect("kd", kd, (B, Hkv, T, Lcap, d), q.dtype, q.device)
+        _expect("vd", vd, (B, Hkv, T, Lcap, d), q.dtype, q.device)
+    if not 0 <= L <= Lcap:
+        raise ValueError(f"L = {L} must lie in [0, {Lcap}]")
+    _check_out(q, out, lse, (B, Hq, T))
+    _check_tensors(q, k, v, kd, vd)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -377,13 +440,19 @@ def fwd_layers(q, k, v, kl=None, vl=None, L=None, *, with_lse: bool = False, out
     """MoDA forward over a layer-major depth stream kl, vl [Lcap,B,Hkv,T,d]: the
     first L slices (default: all) are the depth entries."""
     import torch
-    _check_tensors(q, k, v, kl, vl)
-    B, Hq, T, d = q.shape
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
     if kl is None:
         L = 0
-    elif L is None:
-        L = kl.shape[0]
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    else:
+        Lcap = kl.shape[0]
+        _expect("kl", kl, (Lcap, B, Hkv, T, d), q.dtype, q.device)
+        _expect("vl", vl, (Lcap, B, Hkv, T, d), q.dtype, q.device)
+        L = Lcap if L is None else L
+        if not 0 <= L <= Lcap:
+            raise ValueError(f"L = {L} must lie in [0, {Lcap}]")
+    _check_out(q, out, lse, (B, Hq, T))
+    _check_tensors(q, k, v, kl, vl)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if out is None:
         out = torch.empty_like(q)
     if with_lse and lse is None:
@@ -403,10 +472,26 @@ def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, d
     split, with ``workspace`` (a uint8 device tensor of at least
     moda_bwd_workspace_bytes bytes) or one allocated here; without it, moda_bwd."""
     import torch
-    _check_tensors(q, k, v, out, lse, dout, kd, vd, packed)
-    B, Hq, T, d = q.shape
+    B, Hq, Hkv, T, d = _check_qkv(q, k, v)
     L = 0 if kd is None else kd.shape[3]
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    _expect("out", out, q.shape, q.dtype, q.device)
+    _expect("dout", dout, q.shape, q.dtype, q.device)
+    _expect("lse", lse, (B, Hq, T), torch.float32, q.device)
+    if kd is not None:
+        _expect("kd", kd, (B, Hkv, T, L, d), q.dtype, q.device)
+        _expect("vd", vd, (B, Hkv, T, L, d), q.dtype, q.device)
+    if delta is not None:
+        _expect("delta", delta, (B, Hq, T), torch.float32, q.device)
+    if grads is not None:
+        want = (q.shape, k.shape, v.shape, kd.shape if L else None, vd.shape if L else None)
+        for nm, g, w in zip(("dq", "dk", "dv", "dkd", "dvd"), grads, want):
+            if w is None:
+                if g is not None:
+                    raise ValueError(f"{nm} must be None when L = 0")
+            else:
+                _expect(nm, g, w, q.dtype, q.device)
+    _check_tensors(q, k, v, out, lse, dout, kd, vd, packed)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     if grads is None:
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                  torch.empty_like(kd) if L else None, torch.empty_like(vd) if L else None)
@@ -433,10 +518,17 @@ def bwd(q, k, v, out, lse, dout, kd=None, vd=None, packed=None, *, grads=None, d
 def append_depth(packed, shape: ModaShape, first: int, k_new, v_new):
     """Write entries [first, first + n) of every token into ``packed`` in place;
     k_new, v_new [B,Hkv,T,n,d] (a [B,Hkv,T,d] pair is taken as n = 1)."""
-    _check_tensors(packed, k_new, v_new)
+    if k_new is None or v_new is None or k_new.dim() not in (4, 5):
+        raise ValueError("k_new, v_new must be [B,Hkv,T,d] or [B,Hkv,T,n,d]")
     if k_new.dim() == 4:
         k_new, v_new = k_new.unsqueeze(3), v_new.unsqueeze(3)
     n = k_new.shape[3]
+    want = (shape.B, shape.Hkv, shape.T, n, shape.d)
+    _expect("k_new", k_new, want)
+    _expect("v_new", v_new, want, k_new.dtype, k_new.device)
+    if (shape.dtype == MODA_BF16) != (str(k_new.dtype) == "torch.bfloat16"):
+        raise ValueError(f"k_new dtype {k_new.dtype} does not match the cache shape's dtype")
+    _check_tensors(packed, k_new, v_new)
     _check(moda_append_depth(shape, first, n, _ptr(k_new), _ptr(v_new), _ptr(packed),
                              packed.numel() * packed.element_size(), _stream_ptr(k_new)),
            "moda_append_depth")
@@ -451,11 +543,19 @@ def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=N
     (T is then the capacity).  ``workspace`` may pass a uint8 device tensor of
     at least moda_decode_workspace_bytes bytes."""
     import torch
-    _check_tensors(q, k, v, kd, vd, cache_lens)
+    if q is None or q.dim() != 3 or k is None or k.dim() != 4:
+        raise ValueError("q must be [B,Hq,d] and k [B,Hkv,T,d]")
     B, Hq, d = q.shape
-    T = k.shape[2]
+    Hkv, T = k.shape[1], k.shape[2]
+    _expect("k", k, (B, Hkv, T, d), q.dtype, q.device)
+    _expect("v", v, (B, Hkv, T, d), q.dtype, q.device)
     L = 0 if kd is None else kd.shape[2]
-    shape = make_shape(B, Hq, k.shape[1], T, L, d, q.dtype)
+    if kd is not None:
+        _expect("kd", kd, (B, Hkv, L, d), q.dtype, q.device)
+        _expect("vd", vd, (B, Hkv, L, d), q.dtype, q.device)
+    _check_out(q, out, lse, (B, Hq))
+    _check_tensors(q, k, v, kd, vd, cache_lens)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
     need = moda_decode_workspace_bytes(shape)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -49,12 +49,38 @@ def device_case(cfg, device):
     return torch_inputs(cfg, device)
 
 
-def sample_rows(cfg, n_random=64, seed=0):
-    """Per (b, h): tile-boundary rows plus n_random seeded rows."""
+def tile_rows(variant):
+    """Query rows (token x head pairs) of one workgroup tile of a forward variant
+    (moda_fwd_variant's name): 256 for the 8-wave kernel, 128 for the 4-wave one."""
+    if variant.endswith("_w8"):
+        return 256
+    if variant.endswith("_w4"):
+        return 128
+    raise ValueError(f"no MFMA tile for variant {variant!r}")
+
+
+def seam_tokens(T, G, rows_per_tile):
+    """Tokens on both sides of the kernel's real seams: the first and last tile
+    seams (tiles hold rows_per_tile // G tokens), the seam in the middle of the
+    sequence, one wave seam (32 // G tokens per wave), the start of the last
+    (possibly ragged) tile, and the first and last tokens."""
+    tq = max(1, rows_per_tile // G)
+    wq = max(1, 32 // G)
+    last = ((T - 1) // tq) * tq           # first token of the last tile
+    mid = ((T // 2) // tq) * tq           # a tile seam near the middle
+    ts = {0, 1, T - 1, T // 2}
+    for s in (tq, mid, last, T - tq, wq):
+        ts |= {s - 1, s, s + 1}
+    return {t for t in ts if 0 <= t < T}
+
+
+def sample_rows(cfg, n_random=64, seed=0, rows_per_tile=256):
+    """Per (b, h): the rows on both sides of the forward kernel's tile and wave
+    seams (``rows_per_tile`` from tile_rows of the variant the shape runs)
+    plus n_random seeded rows."""
     B, Hq, Hkv, T = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"]
     G = Hq // Hkv
-    tq = max(1, 128 // G)
-    fixed = {0, 1, tq - 1, tq, tq + 1, T // 2, T - tq - 1, T - tq, T - 1}
+    fixed = seam_tokens(T, G, rows_per_tile)
     rng = np.random.default_rng(seed)
     rows = []
     for b in range(B):

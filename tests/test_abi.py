@@ -236,3 +236,52 @@ def test_binding_refuses_host_tensors(m):
     q = torch.zeros(1, 2, 4, 32)
     with pytest.raises(ValueError):
         m.fwd(q, q[:, :1], q[:, :1])
+
+
+def test_binding_checks_shapes_and_dtypes(m):
+    """The torch conveniences refuse tensors whose shape, dtype or device does
+    not match before anything reaches the C ABI, which gets bare pointers and
+    could not tell a short or mistyped buffer from a good one."""
+    import torch
+    bf = torch.bfloat16
+    B, Hq, Hkv, T, L, d = 1, 8, 2, 16, 3, 128
+    q = torch.zeros(B, Hq, T, d, dtype=bf)
+    k = torch.zeros(B, Hkv, T, d, dtype=bf)
+    v = torch.zeros(B, Hkv, T, d, dtype=bf)
+    kd = torch.zeros(B, Hkv, T, L, d, dtype=bf)
+    vd = torch.zeros(B, Hkv, T, L, d, dtype=bf)
+    short_v = torch.zeros(B, Hkv, T - 1, d, dtype=bf)
+    f32_k = torch.zeros(B, Hkv, T, d, dtype=torch.float32)
+    lse = torch.zeros(B, Hq, T, dtype=torch.float32)
+    cases = [
+        lambda: m.fwd(q, k, short_v),
+        lambda: m.fwd(q, f32_k, v),
+        lambda: m.fwd(q, k, v, out=torch.zeros(B, Hq, T, 64, dtype=bf)),
+        lambda: m.fwd(q, k, v, lse=torch.zeros(B, Hq, T, dtype=bf)),
+        lambda: m.causal_fwd(q, k, short_v),
+        lambda: m.causal_fwd(q, k[:, :, :, :64].contiguous(), v),
+        lambda: m.fwd_natural(q, k, v, kd, vd[:, :, :, :2].contiguous()),
+        lambda: m.fwd_natural(q, k, v, kd.float(), vd),
+        lambda: m.fwd_masked_scan(q, k, v, kd, None),
+        lambda: m.fwd_capacity(q, k, v, kd, vd, L=L + 1),
+        lambda: m.fwd_layers(q, k, v, kd.permute(3, 0, 1, 2, 4).contiguous(),
+                             vd.permute(3, 0, 1, 2, 4).contiguous()[:2]),
+        lambda: m.depth_fwd(q[0], None, Hkv, L),
+        lambda: m.bwd(q, k, v, q, lse, short_v),
+        lambda: m.bwd(q, k, v, q, lse.to(bf), q),
+        lambda: m.bwd(q, k, v, q, lse, q, kd, vd[:, :1].contiguous()),
+        lambda: m.bwd(q, k, v, q, lse, q, grads=(q, k, short_v, None, None)),
+        lambda: m.pack_depth_cache(kd, vd[:, :, :1].contiguous()),
+        lambda: m.pack_depth_cache(kd, vd, m.make_shape(B, Hq, Hkv, T + 1, L, d, "bf16")),
+        lambda: m.append_depth(torch.zeros(8, dtype=torch.uint8),
+                               m.make_shape(B, Hq, Hkv, T, L, d, "bf16"), 0,
+                               k[:, :, :-1].contiguous(), v[:, :, :-1].contiguous()),
+        lambda: m.append_depth(torch.zeros(8, dtype=torch.uint8),
+                               m.make_shape(B, Hq, Hkv, T, L, d, "f32"), 0, k, v),
+        lambda: m.decode(q[:, :, 0], k, short_v),
+        lambda: m.decode(q[:, :, 0], k, v, kd[:, :, 0], vd[:, :, 0, :2].contiguous()),
+        lambda: m.decode(q[:, :, 0], k, v, out=torch.zeros(B, Hq, 64, dtype=bf)),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(ValueError):
+            c()

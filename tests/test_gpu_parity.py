@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 from gpu_util import (BF16_TOL, F32_TOL, LSE_TOL_BF16, LSE_TOL_F32, device_case, gather_rows,
-                      host_case, max_err, oracle_rows_from_device, out_to_f64, sample_rows, to_np)
+                      host_case, max_err, oracle_rows_from_device, out_to_f64, sample_rows,
+                      tile_rows, to_np)
 from synth import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +57,13 @@ def check_full(m, cfg, dev, tol=None, lse_tol=None):
 
 def shape_cfg(B, Hq, Hkv, T, L, d=128, dtype="bf16", scale=1.0, seed=7):
     return dict(B=B, Hq=Hq, Hkv=Hkv, T=T, L=L, d=d, dtype=dtype, scale=scale, seed=seed)
+
+
+def kernel_rows(m, cfg):
+    """Sampled rows of a shape, with the seams of the tile the forward runs it on."""
+    v = m.moda_fwd_variant(m.make_shape(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["L"],
+                                        cfg["d"], cfg["dtype"]))
+    return tile_rows(v)
 
 
 # ------------------------------------------------------------------ full-oracle parity
@@ -113,7 +121,7 @@ def test_layer_1p5b_full(m, dev):
 def sampled_check(m, cfg, dev, n_random=64):
     d_in = device_case(cfg, dev)
     out, lse = run_full(m, d_in, cfg["L"])
-    rows = sample_rows(cfg, n_random=n_random, seed=cfg["seed"])
+    rows = sample_rows(cfg, n_random=n_random, seed=cfg["seed"], rows_per_tile=kernel_rows(m, cfg))
     ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
     got = out_to_f64(gather_rows(out, rows))
     got_l = gather_rows(lse, rows).cpu().numpy()
@@ -219,7 +227,7 @@ def test_fwd_near_size_limit(m, dev):
     assert cfg["T"] * cfg["L"] < 1 << 23
     d_in = device_case(cfg, dev)
     out, lse = run_full(m, d_in, cfg["L"])
-    rows = sample_rows(cfg, n_random=64, seed=cfg["seed"])
+    rows = sample_rows(cfg, n_random=64, seed=cfg["seed"], rows_per_tile=kernel_rows(m, cfg))
     ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
     e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
     e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
@@ -275,7 +283,7 @@ def test_depth_layouts_at_the_index_limit(m, dev):
     torch.cuda.synchronize()
     assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
     del kl, vl, out_l, lse_l
-    rows = sample_rows(cfg, n_random=24, seed=9)
+    rows = sample_rows(cfg, n_random=24, seed=9, rows_per_tile=kernel_rows(m, cfg))
     ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
     e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
     e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
@@ -315,7 +323,7 @@ def test_fwd_layers_stream_prefix(m, dev):
     kl[:l], vl[:l] = layer_major(d_in["kd"]), layer_major(d_in["vd"])
     out, lse = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], kl, vl, l, with_lse=True)
     torch.cuda.synchronize()
-    rows = sample_rows(cfg, n_random=16, seed=5)
+    rows = sample_rows(cfg, n_random=16, seed=5, rows_per_tile=kernel_rows(m, cfg))
     ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
     e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
     e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
