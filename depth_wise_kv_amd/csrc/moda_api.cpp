@@ -179,10 +179,10 @@ size_t decode_ws_bytes(const moda_shape *s) {
   return (size_t)(s->B * s->Hq * decode_splits(s) * moda::kDecodeRecord * 4);
 }
 
-moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
-                        const void *k_cache, const void *v_cache, const void *k_depth,
-                        const void *v_depth, void *out, float *lse, void *workspace,
-                        size_t workspace_bytes, void *hip_stream) {
+// shape and tensor arguments of a decode call (everything but the workspace)
+moda_status decode_check_args(const moda_shape *s, const void *q, const void *k_cache,
+                              const void *v_cache, const void *k_depth, const void *v_depth,
+                              const void *out, const float *lse) {
   moda_status st = check_decode_shape(s);
   if (st != MODA_OK) return st;
   st = check_qkvo(q, k_cache, v_cache, out, lse);
@@ -195,6 +195,15 @@ moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
   } else if (k_depth || v_depth) {
     return fail(MODA_ERR_INVALID_ARG, "depth inputs must be NULL when L == 0");
   }
+  return MODA_OK;
+}
+
+moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
+                        const void *k_cache, const void *v_cache, const void *k_depth,
+                        const void *v_depth, void *out, float *lse, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
+  moda_status st = decode_check_args(s, q, k_cache, v_cache, k_depth, v_depth, out, lse);
+  if (st != MODA_OK) return st;
   if (!workspace || !aligned16(workspace))
     return fail(MODA_ERR_INVALID_ARG, "workspace must be non-NULL and 16-byte aligned");
   const size_t need = decode_ws_bytes(s);
@@ -502,6 +511,26 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
   return decode_impl(s, nullptr, q, k_cache, v_cache, k_depth, v_depth, out, lse, workspace,
                      workspace_bytes, hip_stream);
+}
+
+moda_status moda_decode_noalloc(const moda_shape *s, const int32_t *cache_lens, const void *q,
+                                const void *k_cache, const void *v_cache, const void *k_depth,
+                                const void *v_depth, void *out, float *lse, void *hip_stream) {
+  moda_status st = decode_check_args(s, q, k_cache, v_cache, k_depth, v_depth, out, lse);
+  if (st != MODA_OK) return st;
+  if (cache_lens && ((uintptr_t)cache_lens & 3u) != 0)
+    return fail(MODA_ERR_INVALID_ARG, "cache_lens must be 4-byte aligned");
+  const size_t need = decode_ws_bytes(s);
+  if (need > moda::kDecodeScratchBytes)
+    return fail(MODA_ERR_UNSUPPORTED,
+                "moda_decode_noalloc: the shape needs " + std::to_string(need) +
+                    " bytes of partial states; the static scratch holds " +
+                    std::to_string(moda::kDecodeScratchBytes) + " (use moda_decode)");
+  void *ws = nullptr;
+  const hipError_t e = moda::decode_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "decode scratch lookup");
+  return decode_impl(s, cache_lens, q, k_cache, v_cache, k_depth, v_depth, out, lse, ws,
+                     moda::kDecodeScratchBytes, hip_stream);
 }
 
 moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, const void *q,

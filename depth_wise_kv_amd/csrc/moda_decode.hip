@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moda_device.h"
 #include "moda_internal.h"
 
@@ -270,6 +272,37 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p)
   *(uint32_t *)((__bf16 *)p.out + row * DEC_D + 2 * lane) = cvt_bf16x2(O0 * inv, O1 * inv);
   if (p.lse && lane == 0)
     p.lse[row] = M == -INFINITY ? -INFINITY : (M + __log2f(L)) * 0.69314718055994531f;
+}
+
+// Device scratch of the allocation-free decode (moda_decode_noalloc): its
+// per-part partial states live here instead of in a caller workspace.  Every
+// GPU the library runs on holds one copy for the life of the process; all
+// moda_decode_noalloc calls on a GPU share it, so calls that overlap in time on
+// one GPU race.  The decode writes every record before reading it, so nothing
+// in it needs clearing between calls.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+// Device address of `scratch` on the current device.  Host code may not use
+// the array's name as a device address (it is a host-side stand-in), so the
+// address is looked up once per device, with that device current, and kept.
+hipError_t decode_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecArgs &a, hipStream_t s) {

@@ -99,6 +99,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 // Decode step, bf16, d == 128, G <= 32: partial states, then their merge.
 hipError_t launch_decode(const DecArgs &a, hipStream_t s);
 
+// The allocation-free decode's device scratch: kDecodeScratchBytes bytes per
+// GPU, at the address decode_scratch returns for the current device.
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+hipError_t decode_scratch(void **ptr);
+
 // Depth-stream write into the MFMA block layout (mfma) or the generic one
 // (rows of row_bytes bytes).
 hipError_t launch_append(const AppendArgs &a, bool mfma, int row_bytes, hipStream_t s);

@@ -27,7 +27,7 @@ EXPORTS = ("moda_check_shape", "moda_depth_cache_bytes", "moda_pack_depth_cache"
            "moda_bwd_workspace_bytes", "moda_bwd_ws",
            "moda_decode_workspace_bytes", "moda_decode", "moda_append_depth",
            "moda_fwd_layers", "moda_fwd_masked_scan", "moda_decode_varlen",
-           "moda_fwd_strided",
+           "moda_fwd_strided", "moda_decode_noalloc",
            "moda_status_string", "moda_last_error", "moda_fwd_variant")
 
 
@@ -84,6 +84,8 @@ def _load():
     i64 = ctypes.c_int64
     lib.moda_fwd_strided.argtypes = [sp, vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]
     lib.moda_fwd_strided.restype = ctypes.c_int
+    lib.moda_decode_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moda_decode_noalloc.restype = ctypes.c_int
     lib.moda_fwd_masked_scan.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moda_fwd_masked_scan.restype = ctypes.c_int
     lib.moda_status_string.argtypes = [ctypes.c_int]
@@ -197,6 +199,12 @@ def moda_decode_varlen(shape, lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out
                        ws_ptr, ws_bytes, stream):
     return lib.moda_decode_varlen(_sref(shape), lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr,
                                   out_ptr, lse_ptr, ws_ptr, ws_bytes, stream)
+
+
+def moda_decode_noalloc(shape, lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, out_ptr, lse_ptr,
+                        stream):
+    return lib.moda_decode_noalloc(_sref(shape), lens_ptr, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr,
+                                   out_ptr, lse_ptr, stream)
 
 
 def moda_fwd_strided(shape, q_ptr, k_ptr, v_ptr, kd_ptr, vd_ptr, s_bh, s_t, s_i, out_ptr, lse_ptr,
@@ -573,6 +581,34 @@ def decode(q, k, v, kd=None, vd=None, *, with_lse: bool = False, out=None, lse=N
             raise ValueError("cache_lens must be an int32 tensor of B elements")
         _check(moda_decode_varlen(shape, _ptr(cache_lens), *args), "moda_decode_varlen")
     return (out, lse) if with_lse else out
+
+
+def decode_noalloc(q, k, v, kd=None, vd=None, *, out, lse=None, cache_lens=None):
+    """The decode step through moda_decode_noalloc: the library's fixed device
+    scratch instead of a workspace.  ``out`` (and ``lse``, if wanted) must be
+    given, so that the call allocates nothing."""
+    if q is None or q.dim() != 3 or k is None or k.dim() != 4:
+        raise ValueError("q must be [B,Hq,d] and k [B,Hkv,T,d]")
+    B, Hq, d = q.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    _expect("k", k, (B, Hkv, T, d), q.dtype, q.device)
+    _expect("v", v, (B, Hkv, T, d), q.dtype, q.device)
+    L = 0 if kd is None else kd.shape[2]
+    if kd is not None:
+        _expect("kd", kd, (B, Hkv, L, d), q.dtype, q.device)
+        _expect("vd", vd, (B, Hkv, L, d), q.dtype, q.device)
+    _check_out(q, out, lse, (B, Hq))
+    if out is None:
+        raise ValueError("out is required")
+    if cache_lens is not None and (str(cache_lens.dtype) != "torch.int32" or
+                                   cache_lens.numel() != B):
+        raise ValueError("cache_lens must be an int32 tensor of B elements")
+    _check_tensors(q, k, v, kd, vd, out, lse, cache_lens)
+    shape = make_shape(B, Hq, Hkv, T, L, d, q.dtype)
+    _check(moda_decode_noalloc(shape, _ptr(cache_lens), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(kd if L else None), _ptr(vd if L else None), _ptr(out),
+                               _ptr(lse), _stream_ptr(q)), "moda_decode_noalloc")
+    return out
 
 
 def moda_forward(q, k, v, kd=None, vd=None, *, with_lse: bool = False):

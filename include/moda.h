@@ -323,6 +323,30 @@ moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, c
                                const void *v_depth, void *out, float *lse, void *workspace,
                                size_t workspace_bytes, void *hip_stream);
 
+/* The decode step of moda_decode (cache_lens NULL: every sequence's cache
+ * holds all T entries) or moda_decode_varlen (cache_lens given), with no
+ * workspace argument and no allocation: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The partial states that moda_decode keeps in the
+ * caller's workspace live in a fixed device array of the library instead,
+ * 8 MiB (8388608 bytes) per GPU, held from the first call on a GPU until the
+ * process ends.  The call allocates nothing, neither device nor pinned host
+ * memory; its first call on a GPU looks up the array's device address.
+ *
+ *   cache_lens : NULL, or device int32 [B] as for moda_decode_varlen
+ *   q, k_cache, v_cache, k_depth, v_depth, out, lse : as for moda_decode
+ * Results are those of moda_decode (moda_decode_varlen) on the same inputs,
+ * bit for bit.  A shape whose partial states need more than the array holds
+ * (moda_decode_workspace_bytes(s) > 8388608) is MODA_ERR_UNSUPPORTED, before
+ * any launch; use moda_decode with a workspace for it.  All calls on one GPU
+ * share the array: calls that overlap in time on the same GPU (other streams,
+ * other threads) race and may return wrong results.  The array needs no
+ * clearing: each call writes every partial state before reading it.
+ * Other validation, limits, ownership and asynchrony as for moda_decode. */
+moda_status moda_decode_noalloc(const moda_shape *s, const int32_t *cache_lens, const void *q,
+                                const void *k_cache, const void *v_cache, const void *k_depth,
+                                const void *v_depth, void *out, float *lse, void *hip_stream);
+
 /* Static text of a status code (never NULL). */
 const char *moda_status_string(moda_status st);
 

@@ -188,8 +188,24 @@ int main() {
                                    (float *)p[6], p[8], z[0], nullptr);
        },
        [](const moda_shape *s, size_t *z) { z[0] = moda_decode_workspace_bytes(s); }},
+      {"moda_decode_noalloc", 8, {0, 6}, 0,
+       [](const moda_shape *s, void **p, size_t *) {
+         return moda_decode_noalloc(s, (const int32_t *)p[0], p[1], p[2], p[3], p[4], p[5], p[7],
+                                    (float *)p[6], nullptr);
+       },
+       nullptr},
   };
   for (const auto &c : mfma) check_call(c, bf);
+  {
+    // a shape whose partial states outgrow the static scratch is refused before any launch
+    const moda_shape big = {4096, 128, 4, 64, 0, 128, MODA_BF16};
+    expect(moda_decode_workspace_bytes(&big) > ((size_t)8 << 20), "big decode shape");
+    const int before = g_stub_launches;
+    const moda_status st = moda_decode_noalloc(&big, nullptr, dev(1), dev(2), dev(3), nullptr,
+                                               nullptr, dev(4), nullptr, nullptr);
+    expect(st == MODA_ERR_UNSUPPORTED && g_stub_launches == before,
+           "moda_decode_noalloc refuses a shape beyond its scratch");
+  }
 
   // moda_bwd's unused slot 15 and the workspace variant: a valid split call
   {

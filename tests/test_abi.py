@@ -285,3 +285,26 @@ def test_binding_checks_shapes_and_dtypes(m):
     for i, c in enumerate(cases):
         with pytest.raises(ValueError):
             c()
+
+
+def test_decode_noalloc_rejects_before_launch(m):
+    """moda_decode_noalloc validates on the host like moda_decode, and refuses a
+    shape whose partial states outgrow its fixed 8 MiB scratch, before any GPU call."""
+    p = ctypes.c_void_p(1 << 20)
+    good = m.make_shape(2, 16, 4, 3000, 24, 128, "bf16")
+    assert m.moda_decode_noalloc(None, None, p, p, p, p, p, p, None, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode_noalloc(good, None, None, p, p, p, p, p, None, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode_noalloc(good, None, p, p, p, None, p, p, None, None) == \
+        m.MODA_ERR_INVALID_ARG
+    assert m.moda_decode_noalloc(good, ctypes.c_void_p((1 << 20) + 2), p, p, p, p, p, p, None,
+                                 None) == m.MODA_ERR_INVALID_ARG
+    big = m.make_shape(4096, 128, 4, 64, 0, 128, "bf16")
+    assert m.moda_decode_workspace_bytes(big) > 8 << 20
+    assert m.moda_decode_noalloc(big, None, p, p, p, None, None, p, None, None) == \
+        m.MODA_ERR_UNSUPPORTED
+    assert "scratch" in m.moda_last_error()
+    f32 = m.make_shape(2, 16, 4, 3000, 24, 128, "f32")
+    assert m.moda_decode_noalloc(f32, None, p, p, p, p, p, p, None, None) == \
+        m.MODA_ERR_UNSUPPORTED
