@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/moda.h"
@@ -66,8 +68,11 @@ moda_status check_shape_impl(const moda_shape *s) {
 // without knowing the query head count.
 bool use_mfma(const moda_shape *s) { return s->dtype == MODA_BF16 && s->d == moda::kMfmaD; }
 
+// Blocks of the packed cache per (b, kv head): one per (group of 8 tokens,
+// group of 4 entries).
 int64_t depth_blocks(const moda_shape *s) {
-  return (s->T * s->L + moda::kDepthBlock - 1) / moda::kDepthBlock;
+  return (s->T + moda::kGroupTokens - 1) / moda::kGroupTokens *
+         ((s->L + moda::kGroupEntries - 1) / moda::kGroupEntries);
 }
 
 size_t cache_bytes(const moda_shape *s) {
@@ -97,8 +102,13 @@ moda_status grid_fits(const moda_shape *s) {
 // the 256 CUs at most twice over.  Then the causal tiles' unequal lengths
 // leave CUs idle at the end, and a second, smaller workgroup per CU fills
 // them (18-25% less time at T = 4096, B = 1; no change at 1024 tiles).
+// MODA_FWD_VARIANT=w4 or w8 overrides the choice (for tuning and tests; the
+// 4-wave kernel needs G <= 128).
 int fwd_waves(const moda_shape *s) {
   const int64_t G = s->Hq / s->Hkv, tq = moda::kMfmaRows / G;
+  const char *env = std::getenv("MODA_FWD_VARIANT");
+  if (env && std::strcmp(env, "w8") == 0) return 8;
+  if (env && std::strcmp(env, "w4") == 0 && G <= moda::kMfmaRows / 2) return 4;
   const int64_t tiles = (s->T + tq - 1) / tq * s->B * s->Hkv;
   return (G <= moda::kMfmaRows / 2 && tiles <= 512) ? 4 : 8;
 }
@@ -289,8 +299,10 @@ moda_status moda_append_depth(const moda_shape *s, int64_t first, int64_t n, con
     return fail(MODA_ERR_INVALID_ARG, "packed buffer too small: need " + std::to_string(need) +
                                           " bytes, got " + std::to_string(packed_bytes));
   const int64_t es = s->dtype == MODA_BF16 ? 2 : 4;
-  if ((s->T * n * (use_mfma(s) ? 16 : s->d * es / 16) + 255) / 256 > 0x7FFFFFFFll)
-    return fail(MODA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (use_mfma(s) ? n > 65535 : (s->T * n * (s->d * es / 16) + 255) / 256 > 0x7FFFFFFFll)
+    return fail(MODA_ERR_UNSUPPORTED, use_mfma(s) ? "moda_append_depth writes at most 65535 "
+                                                    "entries per call"
+                                                  : "problem too large for one launch");
   moda::AppendArgs a{k_new, v_new, packed, s->B, s->Hkv, s->T, s->L, depth_blocks(s), first, n};
   return hip_status(moda::launch_append(a, use_mfma(s), (int)(s->d * es), (hipStream_t)hip_stream),
                     "append launch");

@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256) void moda_bwd_kv_reduce(BwdArgs p) {
 // covers DD_SPANS spans of TW = floor(32/G) whole tokens (their G query rows
 // each, 32 rows at most), with two waves per span on one SIMD:
 //   the entry wave (a lane per entry of a 32-entry block) reads the block
-//     (packed K half, natural Vd rows) once and computes S_d = Q Kd^T, P_d,
+//     (natural Kd and Vd rows) once and computes S_d = Q Kd^T, P_d,
 //     dP_d = dO Vd^T and dS_d; it passes the block's K rows and dS_d to the
 //     row wave through LDS, then forms dVd^T = dO^T P_d and dKd^T = Q^T dS_d,
 //     with Q^T and dO^T read transposed from the span's rows stored once in
@@ -721,21 +721,22 @@ __global__ __launch_bounds__(64 * DD_WAVES, 1) void moda_bwd_ddepth(BwdArgs p) {
     // blocks past the span read zeros, and rows the span does not own are
     // dropped.  The loads of the next block then stay counted ahead of this
     // block's stores, and the wait for them never waits for the stores.
-    const char *const pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes;
+    const char *const knat = (const char *)p.kd + bh * TL * (BD * 2);
     const char *const vnat = (const char *)p.vd + bh * TL * (BD * 2);
+    // 32 consecutive entries of the natural [B,Hkv,T,L,d] depth K and V: lane l
+    // takes row l % 32, dims 64*(l/32) + 8*ks .. +7 of each (MFMA operand order)
     auto load_block = [&](int64_t blk, u32x4(&kd)[8], u32x4(&vr)[8])
                           __attribute__((always_inline)) {
       const bool in = blk < blk_hi;
       const int64_t left = TL - blk * kDepthBlock;
       const int vrows = !in ? 0 : left < kDepthBlock ? (int)left : kDepthBlock;
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(pk + blk * kPackedBlockBytes), (short)0, in ? (int)kPackedBlockBytes : 0,
-          0x00020000);
+          (void *)(knat + blk * kDepthBlock * (BD * 2)), (short)0, vrows * (BD * 2), 0x00020000);
       const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(vnat + blk * kDepthBlock * (BD * 2)), (short)0, vrows * (BD * 2), 0x00020000);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        kd[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane * 16 + ks * 1024, 0, 0);
+        kd[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, li * 256 + 128 * lh + 16 * ks, 0, 0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         vr[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, li * 256 + 128 * lh + 16 * ks, 0, 0);

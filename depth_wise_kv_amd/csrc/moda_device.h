@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moda_internal.h"
+
 namespace moda {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -93,6 +95,16 @@ __device__ __forceinline__ int row_swz(int row, int slot) { return slot ^ (row &
 __device__ __forceinline__ int col_swz(int row, int slot) { return slot ^ (4 * (row & 3)); }
 
 
+// Packed depth blocks (bf16, d = 128): 32 rows = 8 consecutive tokens (a token
+// group) x 4 consecutive entries (an entry group).  Block row r is the MFMA row
+// of the K half and the k index of the V half; it holds token tok_of_row(r) of
+// the group and entry ent_of_row(r) of the entry group.  With this order the
+// 8 consecutive k values of a V-half chunk (rows 16kk + 8(j/4) + 4h + j%4,
+// j = 0..7) are one entry of the group's 8 tokens, token j at element j, and an
+// entry written alone fills whole chunks.
+__host__ __device__ constexpr int tok_of_row(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+__host__ __device__ constexpr int ent_of_row(int r) { return ((r >> 4) << 1) | ((r >> 2) & 1); }
+
 struct MfmaState {
   float m;          // reference max of scaled logits (log2 units)
   float lsum;       // this lane's partial sum of 2^(x - m)
@@ -159,6 +171,32 @@ __device__ __forceinline__ void softmax_update(MfmaState &st, const floatx16 *s,
     sum = tile_weights<NB>(s, scale_log2, st.m == -INFINITY ? 0.f : -st.m, pb);
   }
   st.lsum += sum;
+}
+
+// Online-softmax update that moves the reference max to every tile's max
+// (for the HBM-bound depth loop, whose VALU has room for the reduction).  A
+// new running maximum then gets weight exactly 1, so bf16 rounding of the
+// weights never touches the entry that dominates a row.
+template <int NB>
+__device__ __forceinline__ void softmax_update_eager(MfmaState &st, const floatx16 *s,
+                                                     float scale_log2, bf16x8 *pb) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+  const float m_new = fmaxf(pair_max(mx) * scale_log2, st.m);
+  if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+    const float alpha = m_new == st.m ? 1.0f : fast_exp2(st.m - m_new);  // 0 from -inf
+    st.lsum *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+  }
+  st.m = m_new;
+  // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
+  st.lsum += tile_weights<NB>(s, scale_log2, m_new == -INFINITY ? 0.f : -m_new, pb);
 }
 
 }  // namespace moda

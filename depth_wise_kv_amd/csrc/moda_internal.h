@@ -12,6 +12,9 @@ constexpr int kMfmaD = 128;         // head dimension
 constexpr int kMfmaRows = 256;      // query rows (token x head pairs) per 8-wave workgroup
 constexpr int kDepthBlock = 32;     // depth entries per packed block
 constexpr int64_t kPackedBlockBytes = 2 * kDepthBlock * kMfmaD * 2;  // K part + V part
+// a packed block holds kGroupTokens consecutive tokens x kGroupEntries entries
+constexpr int kGroupTokens = 8;
+constexpr int kGroupEntries = 4;
 
 struct FwdArgs {
   const void *q, *k, *v, *packed;

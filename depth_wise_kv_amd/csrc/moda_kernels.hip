@@ -290,12 +290,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
           depth_natural(blk_lo, blk_hi, my_lo);
           return;
         }
+        // packed cache: the blocks of the token groups that hold this wave's
+        // tokens, all entry groups of each (a contiguous run of blocks)
+        const int64_t ne = (L + kGroupEntries - 1) / kGroupEntries;
+        const int64_t pblk_lo = (wt_lo / kGroupTokens) * ne;
+        const int64_t pblk_hi = ((wt_hi - 1) / kGroupTokens + 1) * ne;
         const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
         u32x4 kd[8], vd[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-          kd[ks] = *(const u32x4 *)(pk + blk_lo * kPackedBlockBytes + ks * 1024);
-        for (int64_t blk = blk_lo; blk < blk_hi; ++blk) {
+          kd[ks] = *(const u32x4 *)(pk + pblk_lo * kPackedBlockBytes + ks * 1024);
+        int64_t tg = wt_lo / kGroupTokens, eg = 0;  // token group, entry group of blk
+        for (int64_t blk = pblk_lo; blk < pblk_hi; ++blk) {
           const char *kp = pk + blk * kPackedBlockBytes;
 #pragma unroll
           for (int j = 0; j < 8; ++j) vd[j] = *(const u32x4 *)(kp + BLK_HALF + j * 1024);
@@ -308,21 +314,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
                 __builtin_bit_cast(bf16x8, kd[ks]), qb[ks], sd2[ks & 1], 0, 0, 0);
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
-          if (blk + 1 < blk_hi) {
+          if (blk + 1 < pblk_hi) {
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
               kd[ks] = *(const u32x4 *)(kp + kPackedBlockBytes + ks * 1024);
           }
-          // entry of register rr: blk*32 + 8*(rr/4) + 4*lh + rr%4; keep it iff it
-          // belongs to this row's token
-          // (clamped to [-64, L]: every clamped value keeps the keep/drop decision)
-          int64_t rel64 = blk * kDepthBlock + 4 * lh - my_lo;
-          const int rel = (int)(rel64 < -64 ? -64 : (rel64 > L ? L : rel64));
+          // register rr holds block row 8*(rr/4) + 4*lh + rr%4: token
+          // (rr%4) | ((rr/4)%2) << 2 of the group and entry 4*eg + 2*(rr/8) + lh;
+          // keep it iff that is this row's token and an entry below L (a row of
+          // another group, or an idle row, keeps none)
+          const int64_t tpos64 = tok - kGroupTokens * tg;
+          const int tpos = (int)(tpos64 < 0 || tpos64 >= kGroupTokens ? -1 : tpos64);
+          const int64_t ebase = kGroupEntries * eg + lh;
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
-            if ((unsigned)(8 * (rr >> 2) + (rr & 3) + rel) >= (unsigned)L) sd[0][rr] = -INFINITY;
+            if (tpos != tok_of_row(8 * (rr >> 2) + (rr & 3)) || ebase + 2 * (rr >> 3) >= L)
+              sd[0][rr] = -INFINITY;
+          if (++eg == ne) {
+            eg = 0;
+            ++tg;
+          }
+          // a row's L entries span ceil(L/4) blocks: take each block's max, so
+          // that a dominant entry in a later block still gets weight 1 exactly
           bf16x8 pb[2];
-          softmax_update<1>(st, sd, p.scale_log2, pb);
+          softmax_update_eager<1>(st, sd, p.scale_log2, pb);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -520,14 +535,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   }
 }
 
-// Depth repack into MFMA operand order.  One workgroup per 32-entry block of
-// the flat (token, entry) axis of one (b, kv head):
-//   K half: 8 k-steps x 64 lanes x 16 B; lane l of k-step ks holds entry
+// Depth repack into MFMA operand order.  One workgroup per block of one
+// (b, kv head): 8 tokens x 4 entries, block tg * ceil(L/4) + eg holding tokens
+// 8tg .. 8tg+7 and entries 4eg .. 4eg+3, block row r = (token tok_of_row(r),
+// entry ent_of_row(r)):
+//   K half: 8 k-steps x 64 lanes x 16 B; lane l of k-step ks holds row
 //           l % 32, dims 64*(l/32) + 8*ks .. +7   (the A operand of S^T = K Q^T)
 //   V half: 4 dim blocks x 2 k-steps x 64 lanes x 16 B; lane l of (nb, kk)
-//           holds dim 32*nb + l%32 of entries 16kk + 8*(j/4) + 4*(l/32) + j%4,
-//           j = 0..7 (the A operand of O^T += V^T P^T)
-// Entries past T*L are zero.
+//           holds dim 32*nb + l%32 of rows 16kk + 8*(j/4) + 4*(l/32) + j%4,
+//           j = 0..7, i.e. of entry 4eg + 2kk + l/32 of tokens 0..7 of the
+//           group (the A operand of O^T += V^T P^T)
+// Rows of tokens past T or entries past L are zero.
 constexpr int PK_ROW = D * 2 + 16;  // LDS row stride (bytes) while repacking
 
 __global__ __launch_bounds__(256) void moda_pack_mfma(PackArgs p) {
@@ -537,20 +555,23 @@ __global__ __launch_bounds__(256) void moda_pack_mfma(PackArgs p) {
   const int64_t bh = blockIdx.y;
   const int64_t blk = blockIdx.x;
   const int64_t TL = p.T * p.L;
+  const int64_t ne = (p.L + kGroupEntries - 1) / kGroupEntries;  // entry groups per token
+  const int64_t tg = blk / ne, eg = blk - tg * ne;              // token group, entry group
   const __bf16 *kd = (const __bf16 *)p.kd + bh * TL * D;
   const __bf16 *vd = (const __bf16 *)p.vd + bh * TL * D;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = tid + 256 * i;  // 512 chunks of 16 B per half
-    const int ent = c >> 4, ch = c & 15;
-    const int64_t e = blk * kDepthBlock + ent;
+    const int row = c >> 4, ch = c & 15;
+    const int64_t t = kGroupTokens * tg + tok_of_row(row);
+    const int64_t e = kGroupEntries * eg + ent_of_row(row);
     u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-    if (e < TL) {
-      kv = *(const u32x4 *)(kd + e * D + ch * 8);
-      vv = *(const u32x4 *)(vd + e * D + ch * 8);
+    if (t < p.T && e < p.L) {  // padding rows (past T, or past L) stay zero
+      kv = *(const u32x4 *)(kd + (t * p.L + e) * D + ch * 8);
+      vv = *(const u32x4 *)(vd + (t * p.L + e) * D + ch * 8);
     }
-    *(u32x4 *)(ks_lds + ent * PK_ROW + ch * 16) = kv;
-    *(u32x4 *)(vs_lds + ent * PK_ROW + ch * 16) = vv;
+    *(u32x4 *)(ks_lds + row * PK_ROW + ch * 16) = kv;
+    *(u32x4 *)(vs_lds + row * PK_ROW + ch * 16) = vv;
   }
   __syncthreads();
   char *dst = (char *)p.packed + (bh * p.nblk + blk) * kPackedBlockBytes;

@@ -77,8 +77,12 @@ size_t moda_depth_cache_bytes(const moda_shape *s);
  *   k_depth, v_depth : Kd, Vd [B, Hkv, T, L, d] (read only)
  *   packed           : output, packed_bytes >= moda_depth_cache_bytes(s)
  * The packed format is opaque: a pure function of (shape, library version),
- * bit-exact copies of the inputs plus zero padding.  Pass the identical
- * shape to moda_fwd.  Requires L >= 1.
+ * bit-exact copies of the inputs plus zero padding.  (In this version, for bf16
+ * with d = 128: per (b, kv head), blocks of 8 consecutive tokens x 4
+ * consecutive entries in MFMA operand order, so a query tile's tokens read one
+ * contiguous run of blocks and a single entry of every token can be written in
+ * whole 16-byte chunks.)  Pass the identical shape to moda_fwd.  Requires
+ * L >= 1.
  */
 moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth,
                                   const void *v_depth, void *packed,
@@ -136,7 +140,8 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k,
 
 /* MoDA forward reading the depth keys and values in their natural layout
  * [B, Hkv, T, L, d] instead of the packed cache: the same result as
- * moda_fwd (bit for bit), without a repack.  It measures whether the packed
+ * moda_fwd up to the rounding order of the depth terms (it visits a row's
+ * depth entries in other blocks), without a repack.  It measures whether the packed
  * layout earns its repack (the hyper.ai page on arXiv 2603.15619, section
  * "Hardware-efficient implementation", motivates its chunk- and group-aware
  * depth layouts by the cost of non-contiguous depth reads).
@@ -157,7 +162,7 @@ moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k,
  * and the forward of layer l passes the first l slices with L = l (hyper.ai
  * page on arXiv 2603.15619, section "Depth stream mechanism": the stream
  * grows by what each layer writes, and later layers read all of it).
- * Results are the same as moda_fwd's on the same entries, bit for bit.
+ * Results are the same as moda_fwd_natural's on the same entries, bit for bit.
  *
  *   q, k, v            : as for moda_fwd (read only)
  *   k_layers, v_layers : depth K, V [L, B, Hkv, T, d] (read only; NULL if L == 0);
@@ -193,7 +198,7 @@ moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void 
  * is (T * Lcap, Lcap, 1).  Either lets each layer write its entry in place
  * and the next layer read the stream as it stands (hyper.ai page on arXiv
  * 2603.15619, section "Depth stream mechanism").  Results are the same as
- * moda_fwd's on the same entries, bit for bit; rows outside the L entries are
+ * moda_fwd_natural's on the same entries, bit for bit; rows outside the L entries are
  * never read.
  *
  * Strides are in rows of d elements, each >= 0; every addressed row must lie
@@ -231,7 +236,9 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
  *
  *   q, k, v          : as for moda_fwd (read only)
  *   k_depth, v_depth : depth K, V [B, Hkv, T, L, d] (read only; NULL if L == 0)
- *   packed           : the packed depth cache of the same shape (NULL if L == 0)
+ *   packed           : the packed depth cache of the same shape (NULL if L == 0);
+ *                      validated, not read: the gradients read k_depth and
+ *                      v_depth
  *   out, lse         : O and LSE written by moda_fwd for these inputs (read only)
  *   dout             : dO [B, Hq, T, d] (read only)
  *   dq               : dQ [B, Hq, T, d], written in full

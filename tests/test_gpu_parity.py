@@ -92,6 +92,19 @@ def test_mfma_path_small(m, dev, B, Hq, Hkv, T, L):
     check_full(m, cfg, dev)
 
 
+@pytest.mark.parametrize("variant", ["w4", "w8"])
+@pytest.mark.parametrize("B,Hq,Hkv,T,L", [(2, 8, 2, 1000, 24), (1, 16, 4, 70, 100),
+                                          (1, 8, 1, 300, 40), (1, 32, 4, 513, 0),
+                                          (1, 12, 4, 700, 9)])
+def test_both_wave_counts(m, dev, monkeypatch, variant, B, Hq, Hkv, T, L):
+    """The 4-wave (128-row) and the 8-wave (256-row) kernels on the same shapes,
+    whichever the shape would get by default, against the full oracle."""
+    monkeypatch.setenv("MODA_FWD_VARIANT", variant)
+    assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) == \
+        f"mfma_bf16_d128_{variant}"
+    check_full(m, shape_cfg(B, Hq, Hkv, T, L, seed=57 + T + L), dev)
+
+
 GENERIC_SHAPES = [
     (1, 2, 1, 64, 4, 32, "f32"), (1, 4, 2, 33, 3, 64, "f32"), (2, 4, 1, 70, 0, 128, "f32"),
     (1, 6, 2, 130, 5, 64, "bf16"), (1, 2, 2, 45, 2, 32, "bf16"),
@@ -186,16 +199,21 @@ NATURAL_SHAPES = [(1, 16, 4, 70, 5), (2, 4, 4, 9, 33), (1, 8, 1, 40, 65), (1, 32
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
                          ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
-def test_fwd_natural_matches_packed(m, dev, B, Hq, Hkv, T, L):
-    """moda_fwd_natural (depth K/V read in their natural layout) gives the
-    packed path's O and LSE bit for bit: same operands, same MFMA order."""
+def test_fwd_natural_parity(m, dev, B, Hq, Hkv, T, L):
+    """moda_fwd_natural (depth K/V read in their natural layout) and the packed
+    path both match the full oracle.  (They visit a row's depth entries in
+    different blocks, so they differ in rounding, not in what they compute.)"""
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=700 + T + L)
     d_in = device_case(cfg, dev)
     out, lse = run_full(m, d_in, L)
     out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
                                  with_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
+    ref, rlse = oracle.moda_forward(*(to_np(d_in[n]) for n in ("q", "k", "v", "kd", "vd")))
+    for name, o, l in (("packed", out, lse), ("natural", out_n, lse_n)):
+        e_o, e_l = max_err(out_to_f64(o), ref), max_err(l.cpu().numpy(), rlse)
+        print(f"[parity] {name} {cfg} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+        assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
 
 
 def layer_major(t):
@@ -205,12 +223,14 @@ def layer_major(t):
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
                          ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
-def test_fwd_layers_matches_packed(m, dev, B, Hq, Hkv, T, L):
+def test_fwd_layers_matches_natural(m, dev, B, Hq, Hkv, T, L):
     """moda_fwd_layers (depth stream as per-layer slices [L,B,Hkv,T,d]) gives
-    the packed path's O and LSE bit for bit."""
+    the natural-layout forward's O and LSE bit for bit: the same depth rows
+    reach the same operand registers in the same order."""
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=800 + T + L)
     d_in = device_case(cfg, dev)
-    out, lse = run_full(m, d_in, L)
+    out, lse = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                             with_lse=True)
     out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], layer_major(d_in["kd"]),
                                 layer_major(d_in["vd"]), with_lse=True)
     torch.cuda.synchronize()
@@ -219,9 +239,9 @@ def test_fwd_layers_matches_packed(m, dev, B, Hq, Hkv, T, L):
 
 def test_fwd_near_size_limit(m, dev):
     """T*L just under its 2^23 limit (T = 65536, L = 127, G = 4): the packed
-    forward against the oracle on sampled rows, and the natural-layout and
-    layer-major forwards, whose depth reads span all T*L rows, equal to it bit
-    for bit."""
+    and the natural-layout forwards against the oracle on sampled rows, and the
+    layer-major forward, whose depth reads span all T*L rows like the natural
+    one's, equal to the natural one bit for bit."""
     cfg = dict(B=1, Hq=4, Hkv=1, T=65536, L=127, d=128, dtype="bf16", scale=1.0, seed=6100,
                name="T65536_L127")
     assert cfg["T"] * cfg["L"] < 1 << 23
@@ -234,16 +254,19 @@ def test_fwd_near_size_limit(m, dev):
     print(f"[parity] {cfg['name']} rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}",
           flush=True)
     assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    del out, lse
     out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
                                  with_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
-    del out_n, lse_n
+    e_o = max_err(out_to_f64(gather_rows(out_n, rows)), ref)
+    e_l = max_err(gather_rows(lse_n, rows).cpu().numpy(), rlse)
+    print(f"[parity] {cfg['name']} natural max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
+    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
     out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], layer_major(d_in["kd"]),
                                 layer_major(d_in["vd"]), with_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
-    del d_in, out, lse, out_l, lse_l
+    assert torch.equal(out_n, out_l) and torch.equal(lse_n, lse_l)
+    del d_in, out_n, lse_n, out_l, lse_l
     torch.cuda.empty_cache()
 
 
@@ -266,8 +289,9 @@ def test_fwd_masked_scan_matches_natural(m, dev, B, Hq, Hkv, T, L):
 def test_depth_layouts_at_the_index_limit(m, dev):
     """T * L just below 2^23: the largest depth stream the row-by-row layouts
     take (a 32-bit flat index; a 2 GiB buffer range for the natural layout's
-    V loads).  Packed, natural and layer-major forwards agree bit for bit, and
-    sampled rows (the last tokens included) match the oracle."""
+    V loads).  The natural and layer-major forwards agree bit for bit, and
+    sampled rows (the last tokens included) of both them and the packed path
+    match the oracle."""
     B, Hq, Hkv, T, L = 1, 4, 1, 65535, 128
     assert T * L < (1 << 23) and T * L * 256 > (1 << 30)
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=1234)
@@ -275,33 +299,33 @@ def test_depth_layouts_at_the_index_limit(m, dev):
     out, lse = run_full(m, d_in, L)
     out_n, lse_n = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
                                  with_lse=True)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out_n) and torch.equal(lse, lse_n)
-    del out_n, lse_n
     kl, vl = layer_major(d_in["kd"]), layer_major(d_in["vd"])
     out_l, lse_l = m.fwd_layers(d_in["q"], d_in["k"], d_in["v"], kl, vl, with_lse=True)
     torch.cuda.synchronize()
-    assert torch.equal(out, out_l) and torch.equal(lse, lse_l)
+    assert torch.equal(out_n, out_l) and torch.equal(lse_n, lse_l)
     del kl, vl, out_l, lse_l
     rows = sample_rows(cfg, n_random=24, seed=9, rows_per_tile=kernel_rows(m, cfg))
     ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
-    e_o = max_err(out_to_f64(gather_rows(out, rows)), ref)
-    e_l = max_err(gather_rows(lse, rows).cpu().numpy(), rlse)
-    print(f"[limit] T*L={T * L} rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}", flush=True)
-    assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
-    del d_in, out, lse
+    for name, o, l in (("packed", out, lse), ("natural", out_n, lse_n)):
+        e_o = max_err(out_to_f64(gather_rows(o, rows)), ref)
+        e_l = max_err(gather_rows(l, rows).cpu().numpy(), rlse)
+        print(f"[limit] {name} T*L={T * L} rows={len(rows)} max|dO|={e_o:.3e} "
+              f"max|dLSE|={e_l:.3e}", flush=True)
+        assert e_o <= BF16_TOL and e_l <= LSE_TOL_BF16
+    del d_in, out, lse, out_n, lse_n
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", NATURAL_SHAPES,
                          ids=[f"B{b}Hq{hq}Hkv{hk}T{t}L{l}" for b, hq, hk, t, l in NATURAL_SHAPES])
-def test_fwd_capacity_matches_packed(m, dev, B, Hq, Hkv, T, L):
+def test_fwd_capacity_matches_natural(m, dev, B, Hq, Hkv, T, L):
     """A natural-layout stream with room for 7 more entries per token (the
     spare slots hold NaN): the strided forward over its first L entries gives
-    the packed path's O and LSE bit for bit."""
+    the natural-layout forward's O and LSE bit for bit."""
     cfg = shape_cfg(B, Hq, Hkv, T, L, seed=820 + T + L)
     d_in = device_case(cfg, dev)
-    out, lse = run_full(m, d_in, L)
+    out, lse = m.fwd_natural(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                             with_lse=True)
     cap = L + 7
     kc = torch.full((B, Hkv, T, cap, 128), float("nan"), dtype=torch.bfloat16, device=dev)
     vc = torch.full_like(kc, float("nan"))
@@ -465,27 +489,51 @@ def test_guard_bands(m, dev, dt, d):
 
 
 def unpack_mfma(packed, B, Hkv, T, L):
-    """Invert the bf16/d=128 packed layout on the host (uint16 bit patterns)."""
-    nblk = (T * L + 31) // 32
-    P = to_np(packed).view(np.uint16).reshape(B * Hkv, nblk, 2, 4096)
-    K = P[:, :, 0].reshape(B * Hkv, nblk, 8, 2, 32, 8)        # ks, lh, li, j
-    K = K.transpose(0, 1, 4, 3, 2, 5).reshape(B * Hkv, nblk * 32, 128)
-    V = P[:, :, 1].reshape(B * Hkv, nblk, 4, 2, 2, 32, 2, 4)  # nb, kk, lh, li, ja, jc
-    V = V.transpose(0, 1, 3, 6, 4, 7, 2, 5).reshape(B * Hkv, nblk * 32, 128)
-    return K, V
+    """Decode the bf16/d=128 packed layout on the host (uint16 bit patterns)
+    into natural order [B*Hkv, Tp, Lp, 128], Tp = T rounded up to 8 tokens and
+    Lp = L rounded up to 4 entries (the padding must be zero).  The layout, per
+    (b, kv head): blocks of 8 tokens x 4 entries, block tg * ceil(L/4) + eg of
+    16 KiB (K half, then V half); block row r is token
+    8tg + ((r & 3) | ((r >> 3) & 1) << 2), entry 4eg + 2(r >> 4) + ((r >> 2) & 1).
+    K half: lane l of k-step ks holds row l % 32, dims 64(l/32) + 8ks .. +7.
+    V half: lane l of (nb, kk) holds dim 32nb + l % 32 of rows
+    16kk + 8(j/4) + 4(l/32) + j%4, j = 0..7."""
+    BH, ng, ne = B * Hkv, -(-T // 8), -(-L // 4)
+    nblk = ng * ne
+    P = to_np(packed).view(np.uint16).reshape(BH, nblk, 2, 4096)
+    K = P[:, :, 0].reshape(BH, nblk, 8, 2, 32, 8)        # ks, lh, row, j
+    K = K.transpose(0, 1, 4, 3, 2, 5).reshape(BH, nblk, 32, 128)
+    V = P[:, :, 1].reshape(BH, nblk, 4, 2, 2, 32, 2, 4)  # nb, kk, lh, li, ja, jc
+    V = V.transpose(0, 1, 3, 6, 4, 7, 2, 5).reshape(BH, nblk, 32, 128)  # row = (kk, ja, lh, jc)
+    r = np.arange(32)
+    tok = (r & 3) | (((r >> 3) & 1) << 2)
+    ent = 2 * (r >> 4) + ((r >> 2) & 1)
+    out = []
+    for X in (K, V):
+        X = X.reshape(BH, ng, ne, 32, 128)
+        N = np.zeros((BH, ng, 8, ne, 4, 128), np.uint16)
+        N[:, :, tok, :, ent] = X.transpose(3, 0, 1, 2, 4)  # row r -> (token, entry)
+        out.append(N.reshape(BH, ng * 8, ne * 4, 128))
+    return out
 
 
-@pytest.mark.parametrize("T,L", [(37, 3), (64, 32), (5, 1), (100, 24)])
+def check_unpacked(K, V, kd, vd, T, L):
+    """Decoded cache equals the natural tensors, and every padding row is zero."""
+    BH = K.shape[0]
+    assert np.array_equal(K[:, :T, :L], kd.reshape(BH, T, L, 128))
+    assert np.array_equal(V[:, :T, :L], vd.reshape(BH, T, L, 128))
+    for X in (K, V):
+        assert not X[:, T:].any() and not X[:, :, L:].any()
+
+
+@pytest.mark.parametrize("T,L", [(37, 3), (64, 32), (5, 1), (100, 24), (9, 5), (16, 4)])
 def test_repack_round_trip(m, dev, T, L):
     cfg = shape_cfg(2, 4, 2, T, L, seed=31 + T)
     h_in, d_in = host_case(cfg, dev)
     packed = m.pack_depth_cache(d_in["kd"], d_in["vd"])
     torch.cuda.synchronize()
     K, V = unpack_mfma(packed, 2, 2, T, L)
-    TL = T * L
-    assert np.array_equal(K[:, :TL], h_in["kd"].reshape(4, TL, 128))
-    assert np.array_equal(V[:, :TL], h_in["vd"].reshape(4, TL, 128))
-    assert not K[:, TL:].any() and not V[:, TL:].any()
+    check_unpacked(K, V, h_in["kd"], h_in["vd"], T, L)
 
 
 def test_generic_repack_round_trip(m, dev):
@@ -926,10 +974,7 @@ def test_append_builds_the_cache(m, dev, B, Hkv, T, L, groups):
     ref = m.pack_depth_cache(d_in["kd"], d_in["vd"], shape)
     torch.cuda.synchronize()
     K, V = unpack_mfma(cache, B, Hkv, T, L)
-    TL = T * L
-    assert np.array_equal(K[:, :TL], h_in["kd"].reshape(B * Hkv, TL, 128))
-    assert np.array_equal(V[:, :TL], h_in["vd"].reshape(B * Hkv, TL, 128))
-    assert not K[:, TL:].any() and not V[:, TL:].any()
+    check_unpacked(K, V, h_in["kd"], h_in["vd"], T, L)
     assert torch.equal(cache, ref)
 
 
