@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoda.so")
-SOURCES = ["moda_kernels.hip", "moda_bwd.hip", "moda_decode.hip", "moda_append.hip", "moda_api.cpp"]
+SOURCES = ["moda_kernels.hip", "moda_fwd_small.hip", "moda_bwd.hip", "moda_decode.hip",
+           "moda_append.hip", "moda_api.cpp"]
 ARCH = os.environ.get("MODA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -11,6 +11,7 @@
 
 #include "../../include/moda.h"
 #include "moda_internal.h"
+#include "moda_small.h"
 
 namespace {
 
@@ -68,6 +69,18 @@ moda_status check_shape_impl(const moda_shape *s) {
 // without knowing the query head count.
 bool use_mfma(const moda_shape *s) { return s->dtype == MODA_BF16 && s->d == moda::kMfmaD; }
 
+// The matrix-core kernel for the other head dims and fp32 (moda_fwd_small.hip)
+// serves the rest up to G = 128; the one-wave-per-row VALU kernel only G above.
+bool use_small(const moda_shape *s) {
+  return !use_mfma(s) && moda::small_supported(s->dtype == MODA_BF16, s->d, s->Hq / s->Hkv);
+}
+
+hipError_t launch_fwd_other(const moda_shape *s, const moda::FwdArgs &a, hipStream_t stream) {
+  const bool bf16 = s->dtype == MODA_BF16;
+  return use_small(s) ? moda::launch_fwd_small(a, bf16, stream)
+                      : moda::launch_fwd_generic(a, bf16, stream);
+}
+
 // Blocks of the packed cache per (b, kv head): one per (group of 8 tokens,
 // group of 4 entries).
 int64_t depth_blocks(const moda_shape *s) {
@@ -90,6 +103,8 @@ moda_status grid_fits(const moda_shape *s) {
     if (s->L > 0 && depth_blocks(s) > 0x7FFFFFFFll)
       return fail(MODA_ERR_UNSUPPORTED, "depth cache too long for the pack grid");
     if (s->B * s->Hkv > 65535) return fail(MODA_ERR_UNSUPPORTED, "B * Hkv above 65535");
+  } else if (use_small(s)) {
+    grid = moda::small_grid(s->B, s->Hkv, s->T, s->Hq / s->Hkv);
   } else {
     grid = s->B * s->Hq * s->T;
   }
@@ -259,6 +274,11 @@ size_t moda_depth_cache_bytes(const moda_shape *s) {
 
 const char *moda_fwd_variant(const moda_shape *s) {
   if (check_shape_impl(s) != MODA_OK) return "";
+  if (use_small(s)) {
+    static const char *const names[2][3] = {{"mfma_f32_d32", "mfma_f32_d64", "mfma_f32_d128"},
+                                            {"mfma_bf16_d32", "mfma_bf16_d64", ""}};
+    return names[s->dtype == MODA_BF16][s->d == 32 ? 0 : s->d == 64 ? 1 : 2];
+  }
   if (!use_mfma(s)) return "generic";
   return fwd_waves(s) == 4 ? "mfma_bf16_d128_w4" : "mfma_bf16_d128_w8";
 }
@@ -325,7 +345,7 @@ moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const vo
   hipStream_t stream = (hipStream_t)hip_stream;
   if (use_mfma(s))
     return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), fwd_waves(s), stream), "fwd launch");
-  return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "fwd launch");
+  return hip_status(launch_fwd_other(s, a, stream), "fwd launch");
 }
 
 moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
@@ -341,7 +361,7 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, c
   hipStream_t stream = (hipStream_t)hip_stream;
   if (use_mfma(&s0))
     return hip_status(moda::launch_fwd_mfma(a, (int)(s0.Hq / s0.Hkv), fwd_waves(&s0), stream), "causal launch");
-  return hip_status(moda::launch_fwd_generic(a, s0.dtype == MODA_BF16, stream), "causal launch");
+  return hip_status(launch_fwd_other(&s0, a, stream), "causal launch");
 }
 
 moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packed,
@@ -358,7 +378,7 @@ moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packe
   hipStream_t stream = (hipStream_t)hip_stream;
   if (use_mfma(s))
     return hip_status(moda::launch_fwd_mfma(a, (int)(s->Hq / s->Hkv), fwd_waves(s), stream), "depth launch");
-  return hip_status(moda::launch_fwd_generic(a, s->dtype == MODA_BF16, stream), "depth launch");
+  return hip_status(launch_fwd_other(s, a, stream), "depth launch");
 }
 
 namespace {

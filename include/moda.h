@@ -361,7 +361,14 @@ const char *moda_status_string(moda_status st);
 const char *moda_last_error(void);
 
 /* Kernel variant moda_fwd would launch for `s` (static text, for logging and
- * tests): "mfma_bf16_d128", "generic", or "" if `s` is invalid. Host only. */
+ * tests), or "" if `s` is invalid.  Host only.
+ *   "mfma_bf16_d128_w8", "mfma_bf16_d128_w4": bf16 with d = 128, 8-wave
+ *       (256-row) or 4-wave (128-row) workgroups;
+ *   "mfma_bf16_d32", "mfma_bf16_d64", "mfma_f32_d32", "mfma_f32_d64",
+ *   "mfma_f32_d128": the other dtypes and head dims, G up to 128, on the
+ *       matrix cores;
+ *   "generic": those dtypes and head dims with G above 128, one wave per
+ *       query row on the vector ALUs. */
 const char *moda_fwd_variant(const moda_shape *s);
 
 #ifdef __cplusplus

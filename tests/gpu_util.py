@@ -51,10 +51,14 @@ def device_case(cfg, device):
 
 def tile_rows(variant):
     """Query rows (token x head pairs) of one workgroup tile of a forward variant
-    (moda_fwd_variant's name): 256 for the 8-wave kernel, 128 for the 4-wave one."""
+    (moda_fwd_variant's name): 256 for the 8-wave d = 128 kernel, 128 for its
+    4-wave form and for the kernel of the other head dims and fp32."""
     if variant.endswith("_w8"):
         return 256
     if variant.endswith("_w4"):
+        return 128
+    if variant in ("mfma_bf16_d32", "mfma_bf16_d64", "mfma_f32_d32", "mfma_f32_d64",
+                   "mfma_f32_d128"):
         return 128
     raise ValueError(f"no MFMA tile for variant {variant!r}")
 

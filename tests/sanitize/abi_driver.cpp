@@ -232,7 +232,10 @@ int main() {
   expect(moda_decode_workspace_bytes(nullptr) == 0, "decode workspace of NULL");
   expect(moda_bwd_workspace_bytes(nullptr) == 0, "bwd workspace of NULL");
   for (int st = -1; st < 6; ++st) expect(moda_status_string((moda_status)st) != nullptr, "status");
-  expect(std::strcmp(moda_fwd_variant(&f32), "generic") == 0, "f32 variant");
+  expect(std::strncmp(moda_fwd_variant(&f32), "mfma_f32_d", 10) == 0, "f32 variant");
+  moda_shape wide = f32;  // G above 128: the VALU kernel
+  wide.Hq = 256 * wide.Hkv;
+  expect(std::strcmp(moda_fwd_variant(&wide), "generic") == 0, "f32 variant, G = 256");
 
   if (g_fail) {
     std::fprintf(stderr, "%d expectation(s) failed\n", g_fail);

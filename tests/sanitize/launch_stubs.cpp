@@ -6,6 +6,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "../../depth_wise_kv_amd/csrc/moda_internal.h"
+#include "../../depth_wise_kv_amd/csrc/moda_small.h"
 
 int g_stub_launches = 0;
 
@@ -38,6 +39,9 @@ hipError_t launch_append(const AppendArgs &a, bool, int row_bytes, hipStream_t) 
 }
 hipError_t launch_fwd_generic(const FwdArgs &a, bool, hipStream_t) {
   return a.T < 1 ? hipErrorInvalidValue : reached();
+}
+hipError_t launch_fwd_small(const FwdArgs &a, bool bf16, hipStream_t) {
+  return !small_supported(bf16, a.d, a.Hq / a.Hkv) || a.T < 1 ? hipErrorInvalidValue : reached();
 }
 hipError_t launch_pack_generic(const PackArgs &a, bool, hipStream_t) {
   return a.T < 1 ? hipErrorInvalidValue : reached();

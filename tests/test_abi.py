@@ -65,8 +65,16 @@ def test_depth_cache_bytes(m):
     assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128_w4"
     assert m.moda_fwd_variant(shape(m, T=65536)) == "mfma_bf16_d128_w8"
     assert m.moda_fwd_variant(shape(m, Hq=256, Hkv=1)) == "mfma_bf16_d128_w8"   # G > 128
-    assert m.moda_fwd_variant(shape(m, dtype="f32")) == "generic"
-    assert m.moda_fwd_variant(shape(m, d=64)) == "generic"
+    # the matrix-core kernel for the other head dims and fp32, G <= 128
+    assert m.moda_fwd_variant(shape(m, dtype="f32")) == "mfma_f32_d128"
+    assert m.moda_fwd_variant(shape(m, dtype="f32", d=64)) == "mfma_f32_d64"
+    assert m.moda_fwd_variant(shape(m, dtype="f32", d=32)) == "mfma_f32_d32"
+    assert m.moda_fwd_variant(shape(m, d=64)) == "mfma_bf16_d64"
+    assert m.moda_fwd_variant(shape(m, d=32)) == "mfma_bf16_d32"
+    assert m.moda_fwd_variant(shape(m, d=32, Hq=128, Hkv=1)) == "mfma_bf16_d32"
+    # one-wave-per-row VALU kernel above G = 128
+    assert m.moda_fwd_variant(shape(m, d=32, Hq=256, Hkv=1)) == "generic"
+    assert m.moda_fwd_variant(shape(m, dtype="f32", Hq=256, Hkv=1)) == "generic"
 
 
 def test_status_strings(m):

@@ -69,7 +69,7 @@ def kernel_rows(m, cfg):
 # ------------------------------------------------------------------ full-oracle parity
 
 def test_tiny_workload_fp32(m, dev):
-    """B1 Hq2 Hkv1 T64 d32 L4, fp32 (generic path), whole tensor."""
+    """B1 Hq2 Hkv1 T64 d32 L4, fp32 (matrix-core fp32 kernel), whole tensor."""
     check_full(m, WORKLOADS["tiny"], dev)
 
 
@@ -105,9 +105,8 @@ def test_both_wave_counts(m, dev, monkeypatch, variant, B, Hq, Hkv, T, L):
     check_full(m, shape_cfg(B, Hq, Hkv, T, L, seed=57 + T + L), dev)
 
 
-GENERIC_SHAPES = [
-    (1, 2, 1, 64, 4, 32, "f32"), (1, 4, 2, 33, 3, 64, "f32"), (2, 4, 1, 70, 0, 128, "f32"),
-    (1, 6, 2, 130, 5, 64, "bf16"), (1, 2, 2, 45, 2, 32, "bf16"),
+GENERIC_SHAPES = [  # G above 128: the one-wave-per-row VALU kernel
+    (1, 256, 1, 4, 2, 32, "f32"), (1, 256, 1, 3, 0, 64, "bf16"), (1, 512, 2, 3, 1, 128, "f32"),
 ]
 
 
