@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   auto row_stats = [&](int64_t qt) {
     const int row = lane;
     const int64_t tk = k0 + qt * TQr + row / G;
-    const bool ok = row < TQr * G && tk < T;
+    const bool ok = qt >= 0 && row < TQr * G && tk < T;
     const int64_t qr = ok ? (grp + row % G) * T + tk : 0;
     return RowStats{p.lse[qr], p.delta[qr], ok};
   };
@@ -443,14 +443,17 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   }
   __syncthreads();
   if (qt_lo < n_qt) {
-    dma_tile(qt_lo, rq0, cq0, rg0, cg0);
-    const RowStats r0 = row_stats(qt_lo);
+    dma_tile(n_qt - 1, rq0, cq0, rg0, cg0);
+    const RowStats r0 = row_stats(n_qt - 1);
     if (wave == 0) store_stats(0, r0);
   }
   wait_vmem();
   __syncthreads();
 
-  // query tile qt in buffers of parity P; loads of tile qt+1 are issued first
+  // Query tiles are walked from the last one down: the workgroups of a dispatch
+  // round then read the same query tiles at about the same time, as the forward's
+  // workgroups read the same key tiles, and find them in L2.
+  // Query tile qt in buffers of parity P; loads of tile qt-1 are issued first.
   auto body = [&](int64_t qt, auto parity, auto is_dk) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     constexpr bool DK = decltype(is_dk)::value;
@@ -458,9 +461,9 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
     const char *const qtr = P ? cq1 : cq0;
     const char *const gn = P ? rg1 : rg0;
     const char *const gtr = P ? cg1 : cg0;
-    const bool more = qt + 1 < n_qt;
-    if (more) dma_tile(qt + 1, P ? rq0 : rq1, P ? cq0 : cq1, P ? rg0 : rg1, P ? cg0 : cg1);
-    const RowStats rn = row_stats(qt + 1);
+    const bool more = qt > qt_lo;
+    if (more) dma_tile(qt - 1, P ? rq0 : rq1, P ? cq0 : cq1, P ? rg0 : rg1, P ? cg0 : cg1);
+    const RowStats rn = row_stats(qt - 1);
     const int64_t tq0 = k0 + qt * TQr;  // first token of the tile
     // the tile needs the causal mask unless its first token is at or past
     // this group's last key
@@ -555,12 +558,12 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto run = [&](auto is_dk) __attribute__((always_inline)) {
-    int64_t qt = qt_lo;
-    for (; qt + 1 < n_qt; qt += 2) {
+    int64_t qt = n_qt - 1;
+    for (; qt - 1 >= qt_lo; qt -= 2) {
       body(qt, I0{}, is_dk);
-      body(qt + 1, I1{}, is_dk);
+      body(qt - 1, I1{}, is_dk);
     }
-    if (qt < n_qt) body(qt, I0{}, is_dk);
+    if (qt >= qt_lo) body(qt, I0{}, is_dk);
   };
   if (dk_wave)
     run(std::true_type{});
