@@ -43,6 +43,7 @@ import numpy as np  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA (published)
 METRIC = "MoDA fwd TFLOP/s + % bf16 MFMA peak at T=64K; time ratio vs causal-only"
 KERNEL_SOURCES = [os.path.join(ROOT, "depth_wise_kv_amd", "csrc", f)
                   for f in ("moda_kernels.hip", "moda_device.h", "moda_internal.h")]
@@ -91,7 +92,12 @@ def fwd_kernel_name(c):
     from depth_wise_kv_amd import moda
     v = moda.moda_fwd_variant(moda.make_shape(c["B"], c["Hq"], c["Hkv"], c["T"], c["L"], c["d"],
                                               c["dtype"]))
-    return "moda_fwd_mfma<1, 4>" if v.endswith("_w4") else "moda_fwd_mfma<1, 8>"
+    if v.startswith("mfma_bf16_d128"):
+        return "moda_fwd_mfma<1, 4>" if v.endswith("_w4") else "moda_fwd_mfma<1, 8>"
+    if v.startswith("mfma_"):  # the kernel for the other head dims and fp32
+        e = "float" if c["dtype"] == "f32" else "unsigned short"
+        return f"moda_fwd_small<{e}, {c['d']}, true, {'true' if c['L'] else 'false'}>"
+    return "moda_fwd_generic"
 
 
 def roofline(c, fwd_ms, traffic):
@@ -99,11 +105,11 @@ def roofline(c, fwd_ms, traffic):
     intensity (algorithmic flops per algorithmic HBM byte) is above the ridge
     point of the two published peaks, HBM-bound below it."""
     ai = flops(c) / fused_bytes(c)
-    if ai >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+    peak = PEAK_BF16_TFLOPS if c["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    if ai >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         a = flops(c) / fwd_ms / 1e9
         return {"bound": "mfma", "kernel": fwd_kernel_name(c), "achieved": a,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS,
-                "traffic": traffic}
+                "peak": peak, "unit": "TFLOP/s", "frac": a / peak, "traffic": traffic}
     a = fused_bytes(c) / fwd_ms / 1e6
     return {"bound": "hbm", "kernel": fwd_kernel_name(c), "achieved": a,
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": a / PEAK_HBM_GBS, "traffic": traffic}

@@ -128,3 +128,29 @@ def test_small_merge_identity(m, dev):
     e_o = (merged - out.double()).abs().max().item()
     e_l = (mm + torch.log(a + c) - lse.double()).abs().max().item()
     assert e_o <= F32_TOL and e_l <= LSE_TOL_F32
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,L,d,dt", [(1, 16, 4, 16384, 8, 64, "bf16"),
+                                               (1, 8, 8, 8192, 24, 32, "bf16"),
+                                               (1, 16, 2, 4096, 16, 128, "f32")],
+                         ids=["T16384d64bf16", "T8192d32bf16G1", "T4096d128f32G8"])
+def test_small_sampled_large(m, dev, B, Hq, Hkv, T, L, d, dt):
+    """Larger shapes on sampled rows: the seams of the kernel's 128-row tiles
+    and of its waves, plus seeded random rows, against the oracle row by row."""
+    from gpu_util import device_case, gather_rows, oracle_rows_from_device, sample_rows, tile_rows
+    cfg = cfg_of(B, Hq, Hkv, T, L, d, dt, seed=77 + T + d)
+    v = m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, d, dt))
+    assert v == variant_name(d, dt)
+    d_in = device_case(cfg, dev)
+    out, lse = m.moda_forward(d_in["q"], d_in["k"], d_in["v"], d_in["kd"], d_in["vd"],
+                              with_lse=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, n_random=16, seed=3, rows_per_tile=tile_rows(v))
+    ref, rlse = oracle_rows_from_device(cfg, d_in, rows)
+    got = out_to_f64(gather_rows(out, rows))
+    glse = gather_rows(lse, rows).cpu().numpy()
+    tol, ltol = tols(dt)
+    e_o, e_l = max_err(got, ref), max_err(glse, rlse)
+    print(f"[parity] small sampled {cfg} rows={len(rows)} max|dO|={e_o:.3e} max|dLSE|={e_l:.3e}",
+          flush=True)
+    assert e_o <= tol and e_l <= ltol
