@@ -8,9 +8,10 @@
 //
 // Structure (per workgroup: 4 waves, 128 query rows = floor(128 / G) tokens
 // x G heads, rows folded as in the d = 128 kernel, heaviest causal tile first):
-//   * keys are visited in tiles of 32: the sequence keys 0 .. last token of
-//     the tile, then the flat depth entries of the tile's tokens; every tile is
-//     staged in LDS once and read by all four waves;
+//   * keys are visited in tiles of 64, computed as two halves of 32: the
+//     sequence keys 0 .. last token of the tile, then the flat depth entries of
+//     the tile's tokens; every tile is staged in LDS once and read by all four
+//     waves;
 //   * scores are computed transposed, S^T = K Q^T, so that a lane owns one
 //     query row (lanes l and l ^ 32 share it): row max and row sum are in-lane
 //     work plus one exchange;
@@ -26,7 +27,7 @@
 namespace moda {
 namespace {
 
-constexpr int kSmallKeys = 32;                // keys (or depth entries) per tile
+constexpr int kSmallKeys = 64;  // keys (or depth entries) per tile: two 32-key halves
 
 template <typename E>
 struct Elt;
@@ -44,14 +45,14 @@ struct Elt<uint16_t> {
 // LDS geometry of one tile.
 //   bf16: K rows of 2D bytes padded to 2D + 16 (16-byte fragment reads from 16
 //         different rows fall in distinct banks); V stored transposed, rows of
-//         32 keys (64 bytes) padded to 80, read as 8 consecutive keys of one dim.
+//         64 keys (128 bytes) padded to 144, read as 8 consecutive keys of one dim.
 //   fp32: K rows of D floats padded to D + 1 (32 lanes read one float from 32
 //         rows: distinct banks); V row-major, lanes read consecutive dims.
 template <typename E, int D>
 struct SmallTile {
   static constexpr int kEs = Elt<E>::kBytes;
   static constexpr int kKStride = Elt<E>::kBf16 ? 2 * D + 16 : 4 * (D + 1);
-  static constexpr int kVStride = Elt<E>::kBf16 ? 80 : 4 * D;
+  static constexpr int kVStride = Elt<E>::kBf16 ? 2 * kSmallKeys + 16 : 4 * D;
   static constexpr int kKBytes = kSmallKeys * kKStride;
   static constexpr int kVBytes = Elt<E>::kBf16 ? D * kVStride : kSmallKeys * kVStride;
   static constexpr int kChunksPerRow = D * kEs / 16;
@@ -170,23 +171,23 @@ __global__ __launch_bounds__(64 * kSmallWaves) void moda_fwd_small(FwdArgs p) {
     }
   };
 
-  // ---- one tile of 32 keys for this wave: scores, mask, online softmax, P V
-  // keep(key) says whether key (tile-relative key index k0 + k) joins this row.
-  auto compute = [&](auto keep) {
+  // ---- one 32-key half kh of the tile for this wave: scores, mask, online
+  // softmax, P V.  keep(k) says whether tile key k (0..63) joins this row.
+  auto compute = [&](int kh, auto keep) {
     floatx16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    const int krow = 32 * kh + arow_key;
     if constexpr (BF16) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a =
-            *(const bf16x8 *)(k_lds + arow_key * Tile::kKStride + (16 * ks + 8 * h) * 2);
+        const bf16x8 a = *(const bf16x8 *)(k_lds + krow * Tile::kKStride + (16 * ks + 8 * h) * 2);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], s, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 2; ++ks) {
-        const float a = *(const float *)(k_lds + arow_key * Tile::kKStride + (2 * ks + h) * 4);
+        const float a = *(const float *)(k_lds + krow * Tile::kKStride + (2 * ks + h) * 4);
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qop[ks], s, 0, 0, 0);
       }
     }
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void moda_fwd_small(FwdArgs p) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      xs[i] = keep(key_of_reg<BF16>(i, h)) ? s[i] * sc : -INFINITY;
+      xs[i] = keep(32 * kh + key_of_reg<BF16>(i, h)) ? s[i] * sc : -INFINITY;
       tmax = fmaxf(tmax, xs[i]);
     }
     tmax = pair_max(tmax);
@@ -223,27 +224,28 @@ __global__ __launch_bounds__(64 * kSmallWaves) void moda_fwd_small(FwdArgs p) {
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 a =
-              *(const bf16x8 *)(v_lds + (32 * nb + ln) * Tile::kVStride + (16 * kk + 8 * h) * 2);
+          const bf16x8 a = *(const bf16x8 *)(v_lds + (32 * nb + ln) * Tile::kVStride +
+                                             (32 * kh + 16 * kk + 8 * h) * 2);
           acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[nb], 0, 0, 0);
         }
       }
     } else {
-      // key step s (keys 2 s, 2 s + 1) takes register s
+      // key step ks (keys 2 ks, 2 ks + 1 of the half) takes register ks
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const float a = *(const float *)(v_lds + (2 * ks + h) * Tile::kVStride + (32 * nb + ln) * 4);
+          const float a = *(const float *)(v_lds + (32 * kh + 2 * ks + h) * Tile::kVStride +
+                                           (32 * nb + ln) * 4);
           acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xs[ks], acc[nb], 0, 0, 0);
         }
       }
     }
   };
 
-  // ---- a pass over rows [lo, hi) of (ksrc, vsrc) in tiles of 32; every wave
-  // takes part in the staging and the barriers, and computes the tiles that
-  // touch its rows (has_work(k0)).
+  // ---- a pass over rows [lo, hi) of (ksrc, vsrc) in tiles of 64; every wave
+  // takes part in the staging and the barriers, and computes the 32-key halves
+  // that touch its rows (has_work(first key of the half)).
   auto pass = [&](const E *ksrc, const E *vsrc, int64_t lo, int64_t hi, auto has_work,
                   auto keep_at) {
     const int64_t nt = (hi - lo + kSmallKeys - 1) / kSmallKeys;
@@ -255,7 +257,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void moda_fwd_small(FwdArgs p) {
       store();
       __syncthreads();
       if (j + 1 < nt) prefetch(ksrc, vsrc, k0 + kSmallKeys, hi);
-      if (has_work(k0)) compute([&](int k) { return keep_at(k0 + k); });
+      // the second half only where it holds keys of the pass
+      if (has_work(k0)) compute(0, [&](int k) { return keep_at(k0 + k); });
+      if (k0 + 32 < hi && has_work(k0 + 32)) compute(1, [&](int k) { return keep_at(k0 + k); });
     }
   };
 
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void moda_fwd_small(FwdArgs p) {
       // row iff it is one of the row's own token's L entries
       pass(kdep, vdep, t0 * L, t_end * L,
            [&](int64_t e0) {
-             return w_lo <= w_hi && e0 < (w_hi + 1) * L && e0 + kSmallKeys > w_lo * L;
+             return w_lo <= w_hi && e0 < (w_hi + 1) * L && e0 + 32 > w_lo * L;
            },
            [&](int64_t e) { return (uint64_t)(e - tok * L) < (uint64_t)L; });
     }

@@ -14,11 +14,14 @@
 //                   tile in LDS and one depth span serve all G heads (the
 //                   group-aware indexing of the same section).  QK^T and PV
 //                   run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-//   moda_pack_mfma  repacks [B,Hkv,T,L,d] depth K/V into 32-entry blocks laid
-//                   out in MFMA operand order, K block then V block, so each
-//                   wave streams its depth span with fully contiguous loads.
-//   moda_fwd_generic / moda_copy_generic: plain VALU path for fp32 inputs and
-//                   shapes the MFMA path does not cover.
+//   moda_pack_mfma  repacks [B,Hkv,T,L,d] depth K/V into blocks of 8 tokens x
+//                   4 entries laid out in MFMA operand order, K half then V
+//                   half, so each wave streams its depth span with fully
+//                   contiguous loads.
+//   moda_fwd_generic / moda_copy_generic: one wave per query row on the VALU,
+//                   for fp32 or bf16 with d in {32, 64} when G is above 128
+//                   (below that, moda_fwd_small.hip's matrix-core kernel), and
+//                   the copy that fills their depth layout.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -602,7 +605,7 @@ __global__ __launch_bounds__(256) void moda_pack_mfma(PackArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Generic VALU path (fp32 inputs, or bf16 shapes outside the MFMA path).
+// Generic VALU path (fp32, or bf16 with d in {32, 64}, with G above 128).
 // One wave per query row.  Each lane keeps its own online-softmax state over
 // a strided subset of the row's entries; the 64 states are merged at the end.
 // Depth is read from the generic packed layout: [Kd natural | Vd natural].

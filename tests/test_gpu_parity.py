@@ -941,6 +941,35 @@ def test_decode_graph_replay(m, dev):
         assert torch.equal(out, ref), f"replay {i} differs from the eager result"
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,L,d,dt", [(1, 16, 4, 3000, 24, 128, "bf16"),
+                                               (1, 8, 2, 700, 5, 64, "f32")],
+                         ids=["bf16d128", "f32d64"])
+def test_forward_graph_replay(m, dev, B, Hq, Hkv, T, L, d, dt):
+    """The depth-cache repack and the forward captured in one HIP graph: every
+    replay, with eager work and synchronisations between replays, equals the
+    eager result bit for bit (O and LSE)."""
+    cfg = shape_cfg(B, Hq, Hkv, T, L, d=d, dtype=dt, seed=95 + T)
+    _, d_in = host_case(cfg, dev)
+    shape = m.make_shape(B, Hq, Hkv, T, L, d, dt)
+    packed = m.pack_depth_cache(d_in["kd"], d_in["vd"], shape)
+    ref, rlse = m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, with_lse=True)
+    out = torch.empty_like(ref)
+    lse = torch.empty_like(rlse)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        m.pack_depth_cache(d_in["kd"], d_in["vd"], shape, out=packed)
+        m.fwd(d_in["q"], d_in["k"], d_in["v"], packed, L, out=out, lse=lse)
+    for i in range(3):
+        out.zero_()
+        lse.fill_(7.0)
+        packed.fill_(0x33)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, rlse), f"replay {i} differs"
+
+
 # ------------------------------------------------------------------ depth-stream write
 
 APPEND_SHAPES = [  # (B, Hkv, T, L, group sizes n of the writes, in order of entries)
