@@ -93,7 +93,8 @@ def fwd_kernel_name(c):
     v = moda.moda_fwd_variant(moda.make_shape(c["B"], c["Hq"], c["Hkv"], c["T"], c["L"], c["d"],
                                               c["dtype"]))
     if v.startswith("mfma_bf16_d128"):
-        return "moda_fwd_mfma<1, 4>" if v.endswith("_w4") else "moda_fwd_mfma<1, 8>"
+        return {"w4": "moda_fwd_mfma<1, 4, 128>", "w8": "moda_fwd_mfma<1, 8, 256>",
+                "ks": "moda_fwd_mfma<1, 8, 128>"}[v.rsplit("_", 1)[1]]
     if v.startswith("mfma_"):  # the kernel for the other head dims and fp32
         e = "float" if c["dtype"] == "f32" else "unsigned short"
         return f"moda_fwd_small<{e}, {c['d']}, true, {'true' if c['L'] else 'false'}>"

@@ -116,15 +116,21 @@ moda_status grid_fits(const moda_shape *s) {
 // waves (128 rows, two workgroups per CU) when the 256-row grid would fill
 // the 256 CUs at most twice over.  Then the causal tiles' unequal lengths
 // leave CUs idle at the end, and a second, smaller workgroup per CU fills
-// them (18-25% less time at T = 4096, B = 1; no change at 1024 tiles).
-// MODA_FWD_VARIANT=w4 or w8 overrides the choice (for tuning and tests; the
-// 4-wave kernel needs G <= 128).
+// them (18-25% less time at T = 4096, B = 1; no change at 1024 tiles).  When
+// even the 128-row grid fills the chip's 512 four-wave slots at most once, the
+// heaviest tile alone sets the time; the key-split form runs it on two waves
+// per SIMD (8 waves on 128 rows) and takes 2-10% less time there, but more
+// wherever a CU would run workgroups one after another.
 int fwd_waves(const moda_shape *s) {
   const int64_t G = s->Hq / s->Hkv, tq = moda::kMfmaRows / G;
   const char *env = std::getenv("MODA_FWD_VARIANT");
   if (env && std::strcmp(env, "w8") == 0) return 8;
   if (env && std::strcmp(env, "w4") == 0 && G <= moda::kMfmaRows / 2) return 4;
-  const int64_t tiles = (s->T + tq - 1) / tq * s->B * s->Hkv;
+  if (env && std::strcmp(env, "ks") == 0 && G <= moda::kMfmaRows / 2) return moda::kFwdKeySplit;
+  const int64_t tiles = (s->T + tq - 1) / tq * s->B * s->Hkv;  // of 256 rows
+  const int64_t tq2 = moda::kMfmaRows / 2 / G;  // tokens of a 128-row tile (G <= 128)
+  if (G <= moda::kMfmaRows / 2 && (s->T + tq2 - 1) / tq2 * s->B * s->Hkv <= 512)
+    return moda::kFwdKeySplit;
   return (G <= moda::kMfmaRows / 2 && tiles <= 512) ? 4 : 8;
 }
 
@@ -280,7 +286,8 @@ const char *moda_fwd_variant(const moda_shape *s) {
     return names[s->dtype == MODA_BF16][s->d == 32 ? 0 : s->d == 64 ? 1 : 2];
   }
   if (!use_mfma(s)) return "generic";
-  return fwd_waves(s) == 4 ? "mfma_bf16_d128_w4" : "mfma_bf16_d128_w8";
+  const int w = fwd_waves(s);
+  return w == 4 ? "mfma_bf16_d128_w4" : w == 8 ? "mfma_bf16_d128_w8" : "mfma_bf16_d128_ks";
 }
 
 moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth, const void *v_depth,

@@ -91,8 +91,11 @@ struct AppendArgs {
   int64_t first, n;
 };
 
-// MFMA path: dtype bf16, d == 128, G divides 32.
-// waves = 8 (256 rows per workgroup) or 4 (128 rows); G <= 32 * waves.
+// MFMA path: dtype bf16, d == 128.
+// waves = 8 (256 rows per workgroup) or 4 (128 rows), G <= 32 * waves; or
+// kFwdKeySplit: 8 waves on 128 rows, pairs of waves splitting each key tile
+// (causal and packed MoDA modes; the other modes run the 4-wave kernel), G <= 128.
+constexpr int kFwdKeySplit = 9;
 hipError_t launch_fwd_mfma(const FwdArgs &a, int G, int waves, hipStream_t s);
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t s);
 

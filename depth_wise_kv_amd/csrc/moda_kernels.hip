@@ -115,11 +115,20 @@ __device__ __forceinline__ constexpr int pv_order(int i) { return 4 * (i & 3) + 
 
 // NW waves of 32 query rows each: 8 (one workgroup per CU, two waves per
 // SIMD) or 4 (two workgroups per CU, for grids too small to fill the chip
-// several times over with 256-row tiles).
-template <int MODE, int NW>
+// several times over with 256-row tiles).  With ROWS = 128 and NW = 8 (the
+// key-split form, causal and packed MoDA modes only) the waves pair up:
+// waves 2i and 2i+1 own the same 32 rows, one the first 32 keys of every
+// 64-key tile and one the last 32 (and alternate depth blocks), and merge
+// their softmax states at the end.  A 128-row tile then runs on two waves per
+// SIMD, as the 8-wave kernel does, instead of one.
+template <int MODE, int NW, int ROWS>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   constexpr int NWAVE = NW;                  // waves per workgroup
-  constexpr int MR = 32 * NW;                // query rows per workgroup
+  constexpr int MR = ROWS;                   // query rows per workgroup
+  constexpr bool KS = ROWS < 32 * NW;        // key-split pairs of waves
+  static_assert(!KS || (NW == 8 && ROWS == 128 && (MODE == kModeCausal || MODE == kModeModa)),
+                "the key-split form has 8 waves, 128 rows, causal or packed MoDA mode");
+  constexpr int NKB = KS ? 1 : 2;            // 32-key blocks of each tile a wave takes
   constexpr int DMA_ROWS = NKEY / NWAVE;     // tile rows each wave loads
   constexpr int DMA_INSTR = DMA_ROWS / 4;    // 1 KiB (4-row) load instructions per wave per tile
   static_assert(DMA_INSTR >= 1 && 16 % (2 * DMA_INSTR) == 0, "tile loads must divide the MFMAs");
@@ -142,6 +151,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lh = lane >> 5;
+  const int rw = KS ? wave >> 1 : wave;  // this wave's 32-row block
+  const int kh = KS ? wave & 1 : 0;      // its 32-key half of each tile (key split)
 
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   const int64_t t0 = tile * TQ;
 
   // This lane's query row: row r = token-in-tile * G + head-in-group.
-  const int r = wave * 32 + li;
+  const int r = rw * 32 + li;
   const bool row_used = r < TQ * G;
   const int64_t tok = row_used ? t0 + r / G : T;  // idle rows sit past the end
   const int64_t head = hkv * G + (row_used ? r % G : 0);
@@ -279,8 +290,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   auto depth_part = [&]() {
     if constexpr (HAS_DEPTH) {
       const int64_t L = p.L;
-      const int64_t wt_lo = t0 + (wave * 32) / G;
-      int64_t wt_hi = t0 + (wave * 32 + 31) / G + 1;  // one past the wave's last token
+      const int64_t wt_lo = t0 + (rw * 32) / G;
+      int64_t wt_hi = t0 + (rw * 32 + 31) / G + 1;  // one past the wave's last token
       if (wt_hi > t0 + TQ) wt_hi = t0 + TQ;
       if (wt_hi > T) wt_hi = T;
       if (L > 0 && wt_lo < wt_hi) {
@@ -299,12 +310,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
         const int64_t pblk_lo = (wt_lo / kGroupTokens) * ne;
         const int64_t pblk_hi = ((wt_hi - 1) / kGroupTokens + 1) * ne;
         const char *pk = (const char *)p.packed + bh * p.nblk * kPackedBlockBytes + lane * 16;
+        // a key-split pair of waves takes alternate blocks
+        constexpr int KSTEP = KS ? 2 : 1;
+        const int64_t pblk_first = pblk_lo + kh;
         u32x4 kd[8], vd[8];
+        if (pblk_first < pblk_hi) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          kd[ks] = *(const u32x4 *)(pk + pblk_lo * kPackedBlockBytes + ks * 1024);
-        int64_t tg = wt_lo / kGroupTokens, eg = 0;  // token group, entry group of blk
-        for (int64_t blk = pblk_lo; blk < pblk_hi; ++blk) {
+          for (int ks = 0; ks < 8; ++ks)
+            kd[ks] = *(const u32x4 *)(pk + pblk_first * kPackedBlockBytes + ks * 1024);
+        }
+        // token group, entry group of blk
+        int64_t tg = wt_lo / kGroupTokens + (kh < ne ? 0 : 1), eg = kh < ne ? kh : kh - ne;
+        for (int64_t blk = pblk_first; blk < pblk_hi; blk += KSTEP) {
           const char *kp = pk + blk * kPackedBlockBytes;
 #pragma unroll
           for (int j = 0; j < 8; ++j) vd[j] = *(const u32x4 *)(kp + BLK_HALF + j * 1024);
@@ -317,10 +334,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
                 __builtin_bit_cast(bf16x8, kd[ks]), qb[ks], sd2[ks & 1], 0, 0, 0);
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
-          if (blk + 1 < pblk_hi) {
+          if (blk + KSTEP < pblk_hi) {
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
-              kd[ks] = *(const u32x4 *)(kp + kPackedBlockBytes + ks * 1024);
+              kd[ks] = *(const u32x4 *)(kp + KSTEP * kPackedBlockBytes + ks * 1024);
           }
           // register rr holds block row 8*(rr/4) + 4*lh + rr%4: token
           // (rr%4) | ((rr/4)%2) << 2 of the group and entry 4*eg + 2*(rr/8) + lh;
@@ -333,8 +350,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
           for (int rr = 0; rr < 16; ++rr)
             if (tpos != tok_of_row(8 * (rr >> 2) + (rr & 3)) || ebase + 2 * (rr >> 3) >= L)
               sd[0][rr] = -INFINITY;
-          if (++eg == ne) {
-            eg = 0;
+          eg += KSTEP;
+          while (eg >= ne) {
+            eg -= ne;
             ++tg;
           }
           // a row's L entries span ceil(L/4) blocks: take each block's max, so
@@ -363,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
     // ---------------- sequence part
     const int64_t tok_end = (t0 + TQ < T) ? t0 + TQ : T;
     const int n_kt = (int)((tok_end + NKEY - 1) / NKEY);
-    const int64_t wave_tok_lo = t0 + (wave * 32) / G;
+    const int64_t wave_tok_lo = t0 + (rw * 32) / G;
 
     // direct loads: instruction i of this wave fills tile rows 16*wave + 4i .. +3.
     // Buffer descriptors cover one (b, kv head) of K and of V; the tile offset
@@ -417,14 +435,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
           bf16x8, (u32x4){__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
     };
-    auto mask = [&](floatx16 (&s)[2], int kt) {
-      // key offset within the tile of register rr: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
+    auto mask = [&](floatx16 (&s)[NKB], int kt) {
+      // key offset within the tile of register rr of block kb2: 32*kb2 + 8*(rr/4) + 4*lh + rr%4
       const int lim = (int)max((int64_t)-8, min((int64_t)64, tok - (int64_t)kt * NKEY - 4 * lh));
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int b2 = 0; b2 < NKB; ++b2)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
-          if (32 * kb2 + 8 * (rr >> 2) + (rr & 3) > lim) s[kb2][rr] = -INFINITY;
+          if (32 * (b2 + kh) + 8 * (rr >> 2) + (rr & 3) > lim) s[b2][rr] = -INFINITY;
     };
 
     // start from zeroed buffers: loads of rows past T may leave LDS untouched
@@ -453,39 +471,49 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
       // S^T = K Q^T: the two 32-key chains alternate, K fragments are read four
       // MFMAs ahead and the eight loads of tile j+1 are spread between the
       // MFMAs; sched_barrier fences keep this order.
-      floatx16 s[2];
+      // (key split: this wave's 32-key block kh only, 8 MFMAs)
+      constexpr int NQK = 8 * NKB;
+      // fragment i = 2*ks + kb2 of kfrag for MFMA number n
+      auto qk_frag = [&](int n) { return KS ? 2 * n + kh : n; };
+      floatx16 s[NKB];
       {
         bf16x8 a[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = kfrag(k_rd, i);
+        for (int i = 0; i < 4; ++i) a[i] = kfrag(k_rd, qk_frag(i));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ks = i >> 1, kb2 = i & 1;
+        for (int i = 0; i < NQK; ++i) {
+          const int ks = KS ? i : i >> 1, kb2 = KS ? 0 : i & 1;
           const floatx16 c = ks == 0 ? (floatx16){} : s[kb2];
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], qb[ks], c, 0, 0, 0);
-          if (i + 4 < 16) a[i & 3] = kfrag(k_rd, i + 4);
-          if (i % (16 / (2 * DMA_INSTR)) == 0) dma_one(i / (16 / (2 * DMA_INSTR)), j + 1, k_wr, v_wr);
+          if (i + 4 < NQK) a[i & 3] = kfrag(k_rd, qk_frag(i + 4));
+          if (i % (NQK / (2 * DMA_INSTR)) == 0) dma_one(i / (NQK / (2 * DMA_INSTR)), j + 1, k_wr, v_wr);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       MODA_TRACE(2);  // QK^T
       if constexpr (decltype(masked)::value) mask(s, j);
-      bf16x8 pb[4];
-      softmax_update<2>(st, s, sc, pb);
+      bf16x8 pb[2 * NKB];
+      softmax_update<NKB>(st, s, sc, pb);
       MODA_TRACE(3);  // mask + softmax
       // O^T += V^T P^T: V fragments (two transpose reads each) three MFMAs ahead
+      // (key split: the two 16-key steps 2kh, 2kh+1 of this wave's block, 8 MFMAs)
       {
+        constexpr int NPV = 8 * NKB;
+        auto pv_frag = [&](int n) {  // vfrag index 4*nb + kk of MFMA number n
+          const int f = pv_order(n);
+          return KS ? 4 * (f >> 2) + 2 * kh + (f & 3) : f;
+        };
         bf16x8 a[3];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, pv_order(i));
+        for (int i = 0; i < 3; ++i) a[i] = vfrag(v_rd, pv_frag(i));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < NPV; ++i) {
           const int f = pv_order(i);
           st.acc[f >> 2] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], pb[f & 3], st.acc[f >> 2], 0, 0, 0);
-          if (i + 3 < 16) a[i % 3] = vfrag(v_rd, pv_order(i + 3));
+          if (i + 3 < NPV) a[i % 3] = vfrag(v_rd, pv_frag(i + 3));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -519,9 +547,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
   if (!depth_first) depth_part();
   MODA_TRACE(7);  // depth part
   MODA_TRACE_FLUSH;
+  if constexpr (KS) {
+    // Merge each pair's two states: wave 2i+1 leaves (m, l, O^T) in LDS (the
+    // tile buffers, free after the key loop's last barrier; 16 KiB per pair,
+    // register-major so that a lane's reads and writes are consecutive across
+    // lanes), wave 2i rescales both to the larger reference and adds them.
+    __shared__ float ml_s[4][2][64];
+    float *const xs = (float *)(rw == 0 ? k_lds0 : rw == 1 ? k_lds1 : rw == 2 ? v_lds0 : v_lds1);
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) xs[(16 * nb + rr) * 64 + lane] = st.acc[nb][rr];
+      ml_s[rw][0][lane] = st.m;
+      ml_s[rw][1][lane] = st.lsum;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = ml_s[rw][0][lane], l1 = ml_s[rw][1][lane];
+      const float mm = fmaxf(st.m, m1);
+      // a half that saw no entry of the row has m = -inf and weight 0
+      const float a0 = st.m == -INFINITY ? 0.f : fast_exp2(st.m - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+      st.m = mm;
+      st.lsum = st.lsum * a0 + l1 * a1;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          st.acc[nb][rr] = st.acc[nb][rr] * a0 + xs[(16 * nb + rr) * 64 + lane] * a1;
+    }
+  }
   // ---------------- epilogue: the single normalisation
   const float ltot = pair_sum(st.lsum);
-  if (row_ok) {
+  if (row_ok && kh == 0) {
     const float inv = 1.0f / ltot;
     __bf16 *orow = (__bf16 *)p.out + ((b * p.Hq + head) * T + tok) * D;
 #pragma unroll
@@ -717,24 +777,41 @@ static hipError_t launch_fwd_nw(const FwdArgs &a, int G, hipStream_t s) {
   const int64_t TQ = 32 * NW / G;
   const int64_t ntiles = (a.T + TQ - 1) / TQ;
   const dim3 grid((uint32_t)(ntiles * a.B * a.Hkv)), block(64 * NW);
+  constexpr int R = 32 * NW;
   if (a.kd_nat && a.depth_layers)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaLayers, NW, R>), grid, block, 0, s, a);
   else if (a.kd_nat && a.depth_scan)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaScan, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaScan, NW, R>), grid, block, 0, s, a);
   else if (a.kd_nat)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModaNatural, NW, R>), grid, block, 0, s, a);
   else if (!a.has_seq)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeDepth, NW, R>), grid, block, 0, s, a);
   else if (a.has_depth)
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa, NW, R>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal, NW>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal, NW, R>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+// The key-split form: 8 waves on 128-row tiles (causal and packed MoDA modes;
+// the other modes take the 4-wave kernel on the same tiles).
+static hipError_t launch_fwd_ks(const FwdArgs &a, int G, hipStream_t s) {
+  if (a.kd_nat || !a.has_seq) return launch_fwd_nw<4>(a, G, s);
+  if (G < 1 || G > 128) return hipErrorInvalidValue;
+  const int64_t TQ = 128 / G;
+  const int64_t ntiles = (a.T + TQ - 1) / TQ;
+  const dim3 grid((uint32_t)(ntiles * a.B * a.Hkv)), block(64 * 8);
+  if (a.has_depth)
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeModa, 8, 128>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((moda_fwd_mfma<kModeCausal, 8, 128>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs &a, int G, int waves, hipStream_t s) {
   if (waves == 4) return launch_fwd_nw<4>(a, G, s);
   if (waves == 8) return launch_fwd_nw<8>(a, G, s);
+  if (waves == kFwdKeySplit) return launch_fwd_ks(a, G, s);
   return hipErrorInvalidValue;
 }
 

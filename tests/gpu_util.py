@@ -52,10 +52,10 @@ def device_case(cfg, device):
 def tile_rows(variant):
     """Query rows (token x head pairs) of one workgroup tile of a forward variant
     (moda_fwd_variant's name): 256 for the 8-wave d = 128 kernel, 128 for its
-    4-wave form and for the kernel of the other head dims and fp32."""
+    4-wave and key-split forms and for the kernel of the other head dims and fp32."""
     if variant.endswith("_w8"):
         return 256
-    if variant.endswith("_w4"):
+    if variant.endswith("_w4") or variant.endswith("_ks"):
         return 128
     if variant in ("mfma_bf16_d32", "mfma_bf16_d64", "mfma_f32_d32", "mfma_f32_d64",
                    "mfma_f32_d128"):

@@ -22,7 +22,8 @@ static hipError_t reached() {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs &a, int G, int waves, hipStream_t) {
-  if (G < 1 || (waves != 4 && waves != 8) || a.T < 1) return hipErrorInvalidValue;
+  if (G < 1 || (waves != 4 && waves != 8 && waves != kFwdKeySplit) || a.T < 1)
+    return hipErrorInvalidValue;
   return reached();
 }
 hipError_t launch_pack_mfma(const PackArgs &a, hipStream_t) {

@@ -61,8 +61,14 @@ def test_depth_cache_bytes(m):
     assert m.moda_depth_cache_bytes(shape(m, dtype="f32", d=32, T=64, L=4, Hkv=1, Hq=2)) == \
         2 * 64 * 4 * 32 * 4
     assert m.moda_depth_cache_bytes(shape(m, Hq=15)) == 0
-    # 4-wave workgroups when the 256-row grid fills the chip at most twice over
-    assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128_w4"
+    # the key-split form when the 128-row grid fills the chip's 512 slots at most
+    # once (B1 Hkv4 T4096 G4: 512 tiles); 4-wave workgroups when the 256-row grid
+    # fills it at most twice over
+    assert m.moda_fwd_variant(shape(m)) == "mfma_bf16_d128_ks"
+    assert m.moda_fwd_variant(shape(m, T=4097)) == "mfma_bf16_d128_w4"
+    assert m.moda_fwd_variant(shape(m, B=2)) == "mfma_bf16_d128_w4"
+    assert m.moda_fwd_variant(shape(m, T=8192)) == "mfma_bf16_d128_w4"
+    assert m.moda_fwd_variant(shape(m, T=8193)) == "mfma_bf16_d128_w8"
     assert m.moda_fwd_variant(shape(m, T=65536)) == "mfma_bf16_d128_w8"
     assert m.moda_fwd_variant(shape(m, Hq=256, Hkv=1)) == "mfma_bf16_d128_w8"   # G > 128
     # the matrix-core kernel for the other head dims and fp32, G <= 128

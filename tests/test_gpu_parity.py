@@ -92,13 +92,15 @@ def test_mfma_path_small(m, dev, B, Hq, Hkv, T, L):
     check_full(m, cfg, dev)
 
 
-@pytest.mark.parametrize("variant", ["w4", "w8"])
+@pytest.mark.parametrize("variant", ["w4", "w8", "ks"])
 @pytest.mark.parametrize("B,Hq,Hkv,T,L", [(2, 8, 2, 1000, 24), (1, 16, 4, 70, 100),
                                           (1, 8, 1, 300, 40), (1, 32, 4, 513, 0),
-                                          (1, 12, 4, 700, 9)])
+                                          (1, 12, 4, 700, 9), (1, 2, 1, 257, 3),
+                                          (1, 128, 1, 40, 5), (2, 3, 1, 131, 1)])
 def test_both_wave_counts(m, dev, monkeypatch, variant, B, Hq, Hkv, T, L):
-    """The 4-wave (128-row) and the 8-wave (256-row) kernels on the same shapes,
-    whichever the shape would get by default, against the full oracle."""
+    """The 4-wave (128-row), 8-wave (256-row) and key-split (8 waves on 128 rows)
+    kernels on the same shapes, whichever the shape would get by default,
+    against the full oracle."""
     monkeypatch.setenv("MODA_FWD_VARIANT", variant)
     assert m.moda_fwd_variant(m.make_shape(B, Hq, Hkv, T, L, 128, "bf16")) == \
         f"mfma_bf16_d128_{variant}"

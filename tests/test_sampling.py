@@ -21,6 +21,7 @@ def test_seam_tokens_cover_tile_edges():
 def test_tile_rows_of_variants():
     assert tile_rows("mfma_bf16_d128_w8") == 256
     assert tile_rows("mfma_bf16_d128_w4") == 128
+    assert tile_rows("mfma_bf16_d128_ks") == 128
     assert tile_rows("mfma_f32_d64") == 128
     assert tile_rows("mfma_bf16_d32") == 128
     with pytest.raises(ValueError):
