@@ -44,6 +44,7 @@ import numpy as np  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA (published)
+MALL_BYTES = 256 << 20      # MI355X last-level (Infinity) cache, memory side
 METRIC = "MoDA fwd TFLOP/s + % bf16 MFMA peak at T=64K; time ratio vs causal-only"
 KERNEL_SOURCES = [os.path.join(ROOT, "depth_wise_kv_amd", "csrc", f)
                   for f in ("moda_kernels.hip", "moda_device.h", "moda_internal.h")]
@@ -137,14 +138,57 @@ def load_traffic(name):
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed(fn, steps, stream, graph=True):
+def cold_cache(c):
+    """True when a warm last-level cache could hold a noticeable share of what
+    one call reads (algorithmic bytes between a quarter of it and 16 times it):
+    such calls are timed cold, the cache overwritten before each."""
+    return MALL_BYTES // 4 < fused_bytes(c) < 16 * MALL_BYTES
+
+
+class CacheFlush:
+    """Overwrites the last-level cache (and the L2s) with a 512 MiB fill."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(2 * MALL_BYTES, dtype=torch.uint8, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(self.n & 0xFF)
+
+
+def timed(fn, steps, stream, graph=True, flush=None):
     """Mean duration (ms) of one call of fn, from HIP events recorded on the
     stream the kernels run on, one pair around all timed calls.  A call shorter
     than a millisecond is captured `reps` times into a HIP graph and the graph
     is replayed `steps` times: issued one by one from Python, such calls leave
-    the GPU idle between kernels while the host prepares the next launch."""
+    the GPU idle between kernels while the host prepares the next launch.
+    With `flush`, each call runs after flush() (on the same stream) and is timed
+    by its own event pair; the host enqueues ahead of the GPU, which is busy
+    with the flush, so no launch gap enters the pair (timed without the flush,
+    such pairs agree with the graph replay within 2%).  Calls under a
+    millisecond are timed at least 20 times; the median is reported, since a
+    rare call stalls for milliseconds after the flush."""
     import torch
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if flush is not None:
+        fn()
+        torch.cuda.synchronize()
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        n = steps if a.elapsed_time(b) >= 1.0 else max(steps, 20)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for ea, eb in evs:
+            flush()
+            ea.record(stream)
+            fn()
+            eb.record(stream)
+        torch.cuda.synchronize()
+        return [float(np.median([ea.elapsed_time(eb) for ea, eb in evs]))]
     torch.cuda.synchronize()
     a.record(stream)
     fn()
@@ -370,6 +414,9 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
     packed = (torch.empty(moda.moda_depth_cache_bytes(shape), dtype=torch.uint8, device=dev)
               if L else None)
     out = torch.empty_like(q)
+    # calls whose data a warm 256 MB last-level cache could partly hold are
+    # timed cold (fwd, causal, pack, depth alone, natural and layer-major forms)
+    fl = CacheFlush(dev) if cold_cache(cfg) else None
     torch.cuda.synchronize()
 
     def pack():
@@ -393,19 +440,21 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     # per-kernel durations (HIP events on the stream the kernels run on)
-    fwd_ms = float(np.mean(timed(fwd, steps, stream)))
-    pack_ms = float(np.mean(timed(pack, steps, stream))) if L else 0.0
+    fwd_ms = float(np.mean(timed(fwd, steps, stream, flush=fl)))
+    fwd_warm_ms = float(np.mean(timed(fwd, steps, stream))) if fl else None
+    pack_ms = float(np.mean(timed(pack, steps, stream, flush=fl))) if L else 0.0
     causal_ms = None
     if causal:
         cout = torch.empty_like(q)
         moda.causal_fwd(q, k, v, out=cout)
-        causal_ms = float(np.mean(timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream)))
+        causal_ms = float(np.mean(timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream,
+                                        flush=fl)))
     natural_ms = None
     if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
         nout = torch.empty_like(q)
         moda.fwd_natural(q, k, v, kd, vd, out=nout)
         natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
-                                         steps, stream)))
+                                         steps, stream, flush=fl)))
     scan_ms = None
     if ablation and L and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384:
         # layout ablation: the Flash-compatible masked scan over the flat depth axis
@@ -460,7 +509,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         lout = torch.empty_like(q)
         moda.fwd_layers(q, k, v, kl, vl, out=lout)
         layers_ms = float(np.mean(timed(lambda: moda.fwd_layers(q, k, v, kl, vl, out=lout),
-                                        steps, stream)))
+                                        steps, stream, flush=fl)))
         del kl, vl, lout
     append_ms = None
     if L:
@@ -485,7 +534,7 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         dout = torch.empty_like(q)
         moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout)
         depth_ms = float(np.mean(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
-                                       steps, stream)))
+                                       steps, stream, flush=fl)))
     decode_ms = None
     if cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["Hq"] // cfg["Hkv"] <= 32:
         decode_ms = time_decode(cfg, d_in, steps, stream)
@@ -509,7 +558,9 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         bwd()
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
         del o_b, lse_b, dout, grads, delta, bwd_ws
-    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, pack_ms=pack_ms, causal_ms=causal_ms,
+    del fl
+    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, fwd_warm_ms=fwd_warm_ms, pack_ms=pack_ms,
+               cache="cold" if cold_cache(cfg) else "warm", causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
                append_ms=append_ms, append2_ms=append2_ms, layers_ms=layers_ms,
                scan_ms=scan_ms, pertoken_ms=pertoken_ms,
@@ -659,6 +710,8 @@ def main():
                              with_bwd=args.sweep_bwd, ablation=args.ablation)
             print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
+                              "fwd_warm_cache_ms": r["fwd_warm_ms"],
+                              "kernel_timing_cache": r["cache"],
                               "pack_ms": r["pack_ms"], "causal_ms": r["causal_ms"],
                               "fwd_tflops": flops(c) / r["fwd_ms"] / 1e9,
                               "causal_tflops": flops(c, 0) / r["causal_ms"] / 1e9,
@@ -703,6 +756,8 @@ def main():
                    "T": cfg["T"], "L": cfg["L"], "d": cfg["d"], "inputs": "N(0,1) seeded",
                    "step": "moda_pack_depth_cache + moda_fwd"},
         "fwd_ms": r["fwd_ms"],
+        "fwd_warm_cache_ms": r["fwd_warm_ms"],
+        "kernel_timing_cache": r["cache"],
         "pack_ms": r["pack_ms"],
         "causal_ms": r["causal_ms"],
         "fwd_tflops": fwd_tflops,
