@@ -123,15 +123,20 @@ moda_status grid_fits(const moda_shape *s) {
 // wherever a CU would run workgroups one after another.
 int fwd_waves(const moda_shape *s) {
   const int64_t G = s->Hq / s->Hkv, tq = moda::kMfmaRows / G;
+  const int64_t tiles = (s->T + tq - 1) / tq * s->B * s->Hkv;  // of 256 rows
+  const bool rows128 = G <= moda::kMfmaRows / 2;
+  // tiles of 128 rows (G <= 128): twice the grid of 256-row tiles at most
+  const int64_t tq2 = rows128 ? moda::kMfmaRows / 2 / G : 1;
+  const int64_t tiles2 = (s->T + tq2 - 1) / tq2 * s->B * s->Hkv;
+  // a forced choice (for tests and timing) is taken when its grid fits one launch
   const char *env = std::getenv("MODA_FWD_VARIANT");
   if (env && std::strcmp(env, "w8") == 0) return 8;
-  if (env && std::strcmp(env, "w4") == 0 && G <= moda::kMfmaRows / 2) return 4;
-  if (env && std::strcmp(env, "ks") == 0 && G <= moda::kMfmaRows / 2) return moda::kFwdKeySplit;
-  const int64_t tiles = (s->T + tq - 1) / tq * s->B * s->Hkv;  // of 256 rows
-  const int64_t tq2 = moda::kMfmaRows / 2 / G;  // tokens of a 128-row tile (G <= 128)
-  if (G <= moda::kMfmaRows / 2 && (s->T + tq2 - 1) / tq2 * s->B * s->Hkv <= 512)
-    return moda::kFwdKeySplit;
-  return (G <= moda::kMfmaRows / 2 && tiles <= 512) ? 4 : 8;
+  if (env && rows128 && tiles2 <= 0x7FFFFFFFll) {
+    if (std::strcmp(env, "w4") == 0) return 4;
+    if (std::strcmp(env, "ks") == 0) return moda::kFwdKeySplit;
+  }
+  if (rows128 && tiles2 <= 512) return moda::kFwdKeySplit;
+  return (rows128 && tiles <= 512) ? 4 : 8;
 }
 
 moda_status hip_status(hipError_t e, const char *what) {
