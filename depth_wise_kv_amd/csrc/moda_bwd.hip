@@ -31,11 +31,12 @@
 //                   the sequence part dq wrote): each span of whole tokens
 //                   has a wave per entry orientation and a wave per row
 //                   orientation reading the same depth blocks.
-// The key and query tiles go from global memory straight into LDS.  Each
-// tile is stored twice where it is read both ways: "row-swizzled" (chunk c
-// of row r in slot c ^ (r % 16), for operands that hold 8 dims of one row)
-// and "column-swizzled" (chunk c in slot c ^ 4 (r % 4), for transpose reads
-// that hold 4 rows of one dim).
+// The key and query tiles go from global memory straight into LDS, once each,
+// in a layout (UniFrags) that serves both operand reads without bank
+// conflicts: row reads (operands that hold 8 dims of one row) and transpose
+// reads (4 rows of one dim).  The depth-gradient kernel hands K rows over in
+// the "column-swizzled" layout (chunk c of row r in slot c ^ 4 (r % 4)), which
+// only transpose reads use.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -83,6 +84,50 @@ __device__ __forceinline__ void store_row(__bf16 *row, const floatx16 (&acc)[4],
     }
 }
 
+// One copy of a 64-row tile that serves both kinds of operand read without
+// bank conflicts: chunk c of row r sits in slot c ^ sigma(r), with sigma
+// swapping the two 2-bit fields of r % 16.  The 16 lanes of a row-operand read
+// (16 consecutive rows, one chunk) see 16 distinct slots, and the 16 lanes of
+// a transpose read (rows 4h .. 4h+3 of a 16-row step, chunks 4nb + 2g + b)
+// see 8 distinct slots, two 8-byte halves each.
+__device__ __forceinline__ int uni_sigma(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int uni_swz(int row, int slot) { return slot ^ uni_sigma(row); }
+
+// Per-lane addressing of that layout, with the operands of TileFrags:
+//   rowfrag(buf, i): row 32*(i & 1) + lane%32, dims 64*(lane/32) + 8*(i >> 1) .. +7
+//   colfrag(buf, i): i = 4*nb + kk: dims 32*nb + lane%32, the 8 rows of
+//                    k-step kk in the register order of an MFMA result
+struct UniFrags {
+  int k_row, k_x;
+  int lo[4], hi[4];
+  __device__ explicit UniFrags(int lane) {
+    const int li = lane & 31, lh = lane >> 5;
+    const int sg = uni_sigma(li);  // rows li and li + 32 share it
+    k_row = li * 256 + 16 * ((8 * lh) ^ (sg & 8));
+    k_x = sg & 7;
+    // transpose reads: lane (lg, lq) reads row 4*(lg/2) + lq/4 (and 8 below
+    // it), 8-byte half lq%2 of chunk 4nb + 2(lg%2) + (lq%4)/2
+    const int lg = lane >> 4, lq = lane & 15;
+    const int r0 = 4 * (lg >> 1) + (lq >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int c = 4 * nb + 2 * (lg & 1) + ((lq & 3) >> 1);
+      lo[nb] = r0 * 256 + 16 * uni_swz(r0, c) + 8 * (lq & 1);
+      hi[nb] = (r0 + 8) * 256 + 16 * uni_swz(r0 + 8, c) + 8 * (lq & 1);
+    }
+  }
+  __device__ bf16x8 rowfrag(const char *b, int i) const {
+    return *(const bf16x8 *)(b + k_row + 16 * ((i >> 1) ^ k_x) + (i & 1) * 32 * 256);
+  }
+  __device__ bf16x8 colfrag(const char *b, int i) const {
+    const shortx4 l = lds_read_tr(b + lo[i >> 2] + 16 * (i & 3) * 256);
+    const shortx4 h = lds_read_tr(b + hi[i >> 2] + 16 * (i & 3) * 256);
+    return __builtin_bit_cast(
+        bf16x8, (u32x4){__builtin_bit_cast(u32x2, l)[0], __builtin_bit_cast(u32x2, l)[1],
+                        __builtin_bit_cast(u32x2, h)[0], __builtin_bit_cast(u32x2, h)[1]});
+  }
+};
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -115,18 +160,18 @@ constexpr int DQ_ROWS = 32 * DQ_WAVES;  // 256
 __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQ = DQ_ROWS / G;
-  __shared__ __attribute__((aligned(1024))) char kn0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char kn1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char kt0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char kt1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char vn0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char vn1[BTILE];
+  // K and V tiles of each parity, one copy each in the layout UniFrags reads
+  // both ways (K is read both ways, V by rows)
+  __shared__ __attribute__((aligned(1024))) char a_k0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_k1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_v0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_v1[BTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lh = lane >> 5;
-  const TileFrags fr(lane);
+  const UniFrags fr(lane);
 
   const int64_t T = p.T;
   const int64_t BH = p.B * p.Hkv;
@@ -162,28 +207,25 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   const int n_kt = (int)((tok_end + 63) / 64);
   const int64_t wave_tok_lo = t0 + (wave * 32) / G;
 
-  // Tile loads: this wave fills tile rows 8*wave .. +7 of K (twice: row- and
-  // column-swizzled) and V (row-swizzled); 2 instructions of 4 rows each per
-  // copy.  Rows at or past T read as zeros (descriptor range).
+  // Tile loads: this wave fills tile rows 8*wave .. +7 of K and of V, 2
+  // instructions of 4 rows each per tile.  Rows at or past T read as zeros
+  // (descriptor range).
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.k + bh * T * (BD * 2)), (short)0, (int)(T * (BD * 2)), 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.v + bh * T * (BD * 2)), (short)0, (int)(T * (BD * 2)), 0x00020000);
-  uint32_t off_r[2], off_c[2];
+  uint32_t off_u[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 8 * wave + 4 * i + (lane >> 4);
-    off_r[i] = (uint32_t)(row * 256 + 16 * row_swz(row, lane & 15));
-    off_c[i] = (uint32_t)(row * 256 + 16 * col_swz(row, lane & 15));
+    off_u[i] = (uint32_t)(row * 256 + 16 * uni_swz(row, lane & 15));
   }
-  // load q = 0..5 of tile kt: K row-swizzled, K column-swizzled, V row-swizzled
-  auto dma_one = [&](int qi, int kt, char *kn, char *ktr, char *vn) {
+  // load q = 0..3 of tile kt: K, then V
+  auto dma_one = [&](int qi, int kt, char *kn, char *vn) {
     const uint32_t soff = (uint32_t)kt * BTILE;
     const int i = qi & 1;
-    char *dst = (qi < 2 ? kn : qi < 4 ? ktr : vn) + (8 * wave + 4 * i) * 256;
-    if (qi < 2) dma16(k_rsrc, dst, off_r[i], soff);
-    else if (qi < 4) dma16(k_rsrc, dst, off_c[i], soff);
-    else dma16(v_rsrc, dst, off_r[i], soff);
+    char *dst = (qi < 2 ? kn : vn) + (8 * wave + 4 * i) * 256;
+    dma16(qi < 2 ? k_rsrc : v_rsrc, dst, off_u[i], soff);
   };
   // causal mask of key half kb2 of tile kt: register rr holds key
   // 64*kt + 32*kb2 + 8*(rr/4) + 4*lh + rr%4
@@ -195,27 +237,24 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
   };
 
   for (int o = tid * 16; o < BTILE; o += 64 * DQ_WAVES * 16) {
-    *(u32x4 *)(kn0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(kn1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(kt0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(kt1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(vn0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(vn1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_k0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_k1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_v0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_v1 + o) = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 #pragma unroll
-  for (int qi = 0; qi < 6; ++qi) dma_one(qi, 0, kn0, kt0, vn0);
+  for (int qi = 0; qi < 4; ++qi) dma_one(qi, 0, a_k0, a_v0);
   wait_vmem();
   __syncthreads();
 
   auto body = [&](int j, auto parity, bool masked) {
     constexpr int P = decltype(parity)::value;
-    const char *const kn_rd = P ? kn1 : kn0;
-    const char *const kt_rd = P ? kt1 : kt0;
-    const char *const vn_rd = P ? vn1 : vn0;
-    char *const kn_wr = P ? kn0 : kn1;
-    char *const kt_wr = P ? kt0 : kt1;
-    char *const vn_wr = P ? vn0 : vn1;
+    const char *const kn_rd = P ? a_k1 : a_k0;
+    const char *const kt_rd = kn_rd;
+    const char *const vn_rd = P ? a_v1 : a_v0;
+    char *const kn_wr = P ? a_k0 : a_k1;
+    char *const vn_wr = P ? a_v0 : a_v1;
     // The tile is taken as two halves of 32 keys (kb2), which keeps one
     // half's scores, dP and dS in registers at a time.  The loads of tile
     // j+1 are spread between the first half's MFMAs.
@@ -241,7 +280,7 @@ __global__ __launch_bounds__(64 * DQ_WAVES, 1) void moda_bwd_dq(BwdArgs p) {
         for (int ks = 0; ks < 8; ++ks) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 3], qb[ks], s, 0, 0, 0);
           if (ks + 2 < 8) a[(ks + 2) & 3] = fr.rowfrag(kn_rd, 2 * (ks + 2) + kb2);
-          if (kb2 == 0 && ks < 6) dma_one(ks, j + 1, kn_wr, kt_wr, vn_wr);
+          if (kb2 == 0 && ks < 4) dma_one(ks, j + 1, kn_wr, vn_wr);
           __builtin_amdgcn_sched_barrier(0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 3], gb[ks], dp, 0, 0, 0);
           if (ks + 2 < 8) av[(ks + 2) & 3] = fr.rowfrag(vn_rd, 2 * (ks + 2) + kb2);
@@ -318,20 +357,16 @@ template <bool SPLIT>
 __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int G = (int)(p.Hq / p.Hkv);
   const int TQr = QROWS / G;  // tokens per query tile (G <= 64)
-  // Distinct objects, so that the compiler sees that loads in flight into one
-  // parity's buffers never alias the other parity's being read.  c* hold the
-  // column-swizzled copies (read transposed), r* the row-swizzled ones; the
-  // compiler lays out equally aligned LDS objects in name order, which puts
-  // the c* tiles in the low 64 KiB, where every transposed read reaches its
-  // address through the 16-bit offset field.
-  __shared__ __attribute__((aligned(1024))) char cq0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char cq1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char cg0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char cg1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char rq0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char rq1[BTILE];
-  __shared__ __attribute__((aligned(1024))) char rg0[BTILE];
-  __shared__ __attribute__((aligned(1024))) char rg1[BTILE];
+  // Q and dO tiles of each parity, one copy each in the layout UniFrags reads
+  // both ways.  Distinct objects, so that the compiler sees that loads in
+  // flight into one parity's buffers never alias the other parity's being
+  // read; the compiler lays out equally aligned LDS objects in name order,
+  // which puts these (named to sort first) in the low 64 KiB, where every
+  // read reaches its address through the 16-bit offset field.
+  __shared__ __attribute__((aligned(1024))) char a_g0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_g1[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_q0[BTILE];
+  __shared__ __attribute__((aligned(1024))) char a_q1[BTILE];
   __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];  // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];  // -D
   // P of the tile as the dV wave's bf16 B operands: [group][block][k-step][lane]
@@ -341,7 +376,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31, lh = lane >> 5;
-  const TileFrags fr(lane);
+  const UniFrags fr(lane);
   // waves kg and kg + 4 share a SIMD and the key group kg: the first
   // accumulates dV (from S and P), the second dK (from S, dP and dS)
   const int kg = wave % KV_GROUPS;
@@ -380,9 +415,9 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const int64_t n_qt = qt_lo + chunk < n_all ? qt_lo + chunk : n_all;  // one past the last
 
   // Tile loads.  Tile row r holds token t0 + r / G of head hkv*G + r % G; this
-  // wave loads rows KV_ROWS*wave .. +KV_ROWS-1 of Q and of dO, each twice
-  // (row- and column-swizzled), in instructions of 4 rows.  Rows past the
-  // tile's tokens point outside the descriptor range and read as zeros.
+  // wave loads rows KV_ROWS*wave .. +KV_ROWS-1 of Q and of dO in instructions
+  // of 4 rows.  Rows past the tile's tokens point outside the descriptor range
+  // and read as zeros.
   const int64_t grp = b * p.Hq + hkv * G;  // first query head row block of the group
   const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.q + grp * T * (BD * 2)), (short)0, (int)(G * T * (BD * 2)),
@@ -390,24 +425,21 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((const char *)p.dout + grp * T * (BD * 2)), (short)0, (int)(G * T * (BD * 2)),
       0x00020000);
-  uint32_t off_r[KV_DMA], off_c[KV_DMA];
+  uint32_t off_u[KV_DMA];
 #pragma unroll
   for (int i = 0; i < KV_DMA; ++i) {
     const int row = KV_ROWS * wave + 4 * i + (lane >> 4);
     const bool used = row < TQr * G;
     const uint32_t base = (uint32_t)(((row % G) * T + row / G) * 256);
-    off_r[i] = used ? base + 16 * row_swz(row, lane & 15) : 0x80000000u;
-    off_c[i] = used ? base + 16 * col_swz(row, lane & 15) : 0x80000000u;
+    off_u[i] = used ? base + 16 * uni_swz(row, lane & 15) : 0x80000000u;
   }
-  auto dma_tile = [&](int64_t qt, char *qn, char *qtr, char *gn, char *gtr) {
+  auto dma_tile = [&](int64_t qt, char *qn, char *gn) {
     const uint32_t soff = (uint32_t)((k0 + qt * TQr) * 256);
 #pragma unroll
     for (int i = 0; i < KV_DMA; ++i) {
       const int lrow = (KV_ROWS * wave + 4 * i) * 256;
-      dma16(q_rsrc, qn + lrow, off_r[i], soff);
-      dma16(q_rsrc, qtr + lrow, off_c[i], soff);
-      dma16(g_rsrc, gn + lrow, off_r[i], soff);
-      dma16(g_rsrc, gtr + lrow, off_c[i], soff);
+      dma16(q_rsrc, qn + lrow, off_u[i], soff);
+      dma16(g_rsrc, gn + lrow, off_u[i], soff);
     }
   };
   // lse and D of tile row `lane`, loaded by every wave without a branch (rows
@@ -432,18 +464,14 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   };
 
   for (int o = tid * 16; o < BTILE; o += 64 * KV_WAVES * 16) {
-    *(u32x4 *)(rq0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(rq1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(cq0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(cq1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(rg0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(rg1 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(cg0 + o) = u32x4{0, 0, 0, 0};
-    *(u32x4 *)(cg1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_q0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_q1 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_g0 + o) = u32x4{0, 0, 0, 0};
+    *(u32x4 *)(a_g1 + o) = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
   if (qt_lo < n_qt) {
-    dma_tile(n_qt - 1, rq0, cq0, rg0, cg0);
+    dma_tile(n_qt - 1, a_q0, a_g0);
     const RowStats r0 = row_stats(n_qt - 1);
     if (wave == 0) store_stats(0, r0);
   }
@@ -457,12 +485,10 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   auto body = [&](int64_t qt, auto parity, auto is_dk) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     constexpr bool DK = decltype(is_dk)::value;
-    const char *const qn = P ? rq1 : rq0;
-    const char *const qtr = P ? cq1 : cq0;
-    const char *const gn = P ? rg1 : rg0;
-    const char *const gtr = P ? cg1 : cg0;
+    const char *const qn = P ? a_q1 : a_q0;
+    const char *const gn = P ? a_g1 : a_g0;
     const bool more = qt > qt_lo;
-    if (more) dma_tile(qt - 1, P ? rq0 : rq1, P ? cq0 : cq1, P ? rg0 : rg1, P ? cg0 : cg1);
+    if (more) dma_tile(qt - 1, P ? a_q0 : a_q1, P ? a_g0 : a_g1);
     const RowStats rn = row_stats(qt - 1);
     const int64_t tq0 = k0 + qt * TQr;  // first token of the tile
     // the tile needs the causal mask unless its first token is at or past
@@ -550,7 +576,7 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
           acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              fr.colfrag(DK ? qtr : gtr, 4 * nb + 2 * sb + kk), wb[sb][kk], acc[nb], 0, 0, 0);
+              fr.colfrag(DK ? qn : gn, 4 * nb + 2 * sb + kk), wb[sb][kk], acc[nb], 0, 0, 0);
     wait_vmem();
     if (more && wave == 0) store_stats(P ^ 1, rn);
     __syncthreads();
