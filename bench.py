@@ -159,66 +159,60 @@ class CacheFlush:
 
 
 def timed(fn, steps, stream, graph=True, flush=None):
-    """Mean duration (ms) of one call of fn, from HIP events recorded on the
-    stream the kernels run on, one pair around all timed calls.  A call shorter
-    than a millisecond is captured `reps` times into a HIP graph and the graph
-    is replayed `steps` times: issued one by one from Python, such calls leave
-    the GPU idle between kernels while the host prepares the next launch.
-    With `flush`, each call runs after flush() (on the same stream) and is timed
-    by its own event pair; the host enqueues ahead of the GPU, which is busy
-    with the flush, so no launch gap enters the pair (timed without the flush,
-    such pairs agree with the graph replay within 2%).  Calls under a
-    millisecond are timed at least 20 times; the median is reported, since a
-    rare call stalls for milliseconds after the flush."""
+    """Durations (ms) of one call of fn, one sample per timed call or replay,
+    from HIP events recorded on the stream the kernels run on.  Callers report
+    the median (and the minimum where it is shown).
+    - Calls of a millisecond or more: at least max(steps, 20) calls back to
+      back, each between its own event pair.
+    - Shorter calls, warm: `reps` calls are captured into a HIP graph and the
+      graph is replayed max(steps, 100 // reps, 5) times, each replay between
+      its own pair (issued one by one from Python, such calls would leave the
+      GPU idle between kernels while the host prepares the next launch); the
+      replays are timed twice and the second pass kept, since a process's
+      first timed pass runs slow.  A sample is a replay's time over reps.
+    - With `flush` (cold): each call runs after flush() on the same stream,
+      at least max(steps, 20) calls (100 when under a millisecond), each
+      between its own pair; the host enqueues ahead of the GPU, which is busy
+      with the flush, so no launch gap enters the pair (timed that way without
+      the flush, the pairs agree with the graph replay within 2%)."""
     import torch
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if flush is not None:
-        fn()
-        torch.cuda.synchronize()
-        a.record(stream)
-        fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        n = steps if a.elapsed_time(b) >= 1.0 else max(steps, 20)
+
+    def pairs(n, body, before=None):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
         for ea, eb in evs:
-            flush()
+            if before is not None:
+                before()
             ea.record(stream)
-            fn()
+            body()
             eb.record(stream)
         torch.cuda.synchronize()
-        return [float(np.median([ea.elapsed_time(eb) for ea, eb in evs]))]
-    torch.cuda.synchronize()
-    a.record(stream)
+        return np.array([ea.elapsed_time(eb) for ea, eb in evs])
+
     fn()
-    b.record(stream)
     torch.cuda.synchronize()
-    est = a.elapsed_time(b)
+    est = float(pairs(1, fn)[0])
+    if flush is not None:
+        return pairs(max(steps, 20 if est >= 1.0 else 100), fn, flush)
     if graph and est < 1.0:
         reps = max(1, min(200, int(np.ceil(1.0 / max(est, 5e-3)))))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(reps):
                 fn()
-        # the first timed pass in a process runs slow (one-time costs of the
-        # first graphs, clocks ramping up): time two passes, report the second
-        for _ in range(2):
-            a.record(stream)
-            for _ in range(steps):
-                g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
+        n = max(steps, 100 // reps, 5)
+        pairs(n, g.replay)
+        t = pairs(n, g.replay) / reps
         del g
-        return [a.elapsed_time(b) / (steps * reps)]
-    fn()
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(steps):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) / steps]
+        return t
+    return pairs(max(steps, 20), fn)
+
+
+def center(t, cold):
+    """The duration a timing reports: the mean of warm samples (the average
+    launch duration), the median of cold ones (a rare call after the cache
+    overwrite stalls for milliseconds)."""
+    return float(np.median(t) if cold else np.mean(t))
 
 
 def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
@@ -440,21 +434,24 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     # per-kernel durations (HIP events on the stream the kernels run on)
-    fwd_ms = float(np.mean(timed(fwd, steps, stream, flush=fl)))
-    fwd_warm_ms = float(np.mean(timed(fwd, steps, stream))) if fl else None
-    pack_ms = float(np.mean(timed(pack, steps, stream, flush=fl))) if L else 0.0
-    causal_ms = None
+    cold = fl is not None
+    fwd_t = timed(fwd, steps, stream, flush=fl)
+    fwd_ms = center(fwd_t, cold)
+    fwd_median_ms, fwd_min_ms = float(np.median(fwd_t)), float(np.min(fwd_t))
+    fwd_warm_ms = float(np.mean(timed(fwd, steps, stream))) if cold else None
+    pack_ms = center(timed(pack, steps, stream, flush=fl), cold) if L else 0.0
+    causal_ms = causal_min_ms = None
     if causal:
         cout = torch.empty_like(q)
         moda.causal_fwd(q, k, v, out=cout)
-        causal_ms = float(np.mean(timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream,
-                                        flush=fl)))
+        causal_t = timed(lambda: moda.causal_fwd(q, k, v, out=cout), steps, stream, flush=fl)
+        causal_ms, causal_min_ms = center(causal_t, cold), float(np.min(causal_t))
     natural_ms = None
     if L and cfg["dtype"] == "bf16" and cfg["d"] == 128:
         nout = torch.empty_like(q)
         moda.fwd_natural(q, k, v, kd, vd, out=nout)
-        natural_ms = float(np.mean(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
-                                         steps, stream, flush=fl)))
+        natural_ms = center(timed(lambda: moda.fwd_natural(q, k, v, kd, vd, out=nout),
+                                  steps, stream, flush=fl), cold)
     scan_ms = None
     if ablation and L and cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["T"] <= 16384:
         # layout ablation: the Flash-compatible masked scan over the flat depth axis
@@ -508,8 +505,8 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         vl = vd.permute(3, 0, 1, 2, 4).contiguous()
         lout = torch.empty_like(q)
         moda.fwd_layers(q, k, v, kl, vl, out=lout)
-        layers_ms = float(np.mean(timed(lambda: moda.fwd_layers(q, k, v, kl, vl, out=lout),
-                                        steps, stream, flush=fl)))
+        layers_ms = center(timed(lambda: moda.fwd_layers(q, k, v, kl, vl, out=lout),
+                                 steps, stream, flush=fl), cold)
         del kl, vl, lout
     append_ms = None
     if L:
@@ -533,8 +530,8 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
     if L:
         dout = torch.empty_like(q)
         moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout)
-        depth_ms = float(np.mean(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
-                                       steps, stream, flush=fl)))
+        depth_ms = center(timed(lambda: moda.depth_fwd(q, packed, cfg["Hkv"], L, out=dout),
+                                steps, stream, flush=fl), cold)
     decode_ms = None
     if cfg["dtype"] == "bf16" and cfg["d"] == 128 and cfg["Hq"] // cfg["Hkv"] <= 32:
         decode_ms = time_decode(cfg, d_in, steps, stream)
@@ -559,7 +556,9 @@ def bench_config(cfg, steps, warmup, with_cpu, causal=True, with_bwd=True, ablat
         bwd_ms = float(np.mean(timed(bwd, steps, stream)))
         del o_b, lse_b, dout, grads, delta, bwd_ws
     del fl
-    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, fwd_warm_ms=fwd_warm_ms, pack_ms=pack_ms,
+    res = dict(wall_ms=wall_ms, fwd_ms=fwd_ms, fwd_median_ms=fwd_median_ms, fwd_min_ms=fwd_min_ms,
+               causal_min_ms=causal_min_ms,
+               fwd_warm_ms=fwd_warm_ms, pack_ms=pack_ms,
                cache="cold" if cold_cache(cfg) else "warm", causal_ms=causal_ms,
                depth_ms=depth_ms, bwd_ms=bwd_ms, natural_ms=natural_ms, decode_ms=decode_ms,
                append_ms=append_ms, append2_ms=append2_ms, layers_ms=layers_ms,
@@ -756,10 +755,13 @@ def main():
                    "T": cfg["T"], "L": cfg["L"], "d": cfg["d"], "inputs": "N(0,1) seeded",
                    "step": "moda_pack_depth_cache + moda_fwd"},
         "fwd_ms": r["fwd_ms"],
+        "fwd_median_ms": r["fwd_median_ms"],
+        "fwd_min_ms": r["fwd_min_ms"],
         "fwd_warm_cache_ms": r["fwd_warm_ms"],
         "kernel_timing_cache": r["cache"],
         "pack_ms": r["pack_ms"],
         "causal_ms": r["causal_ms"],
+        "causal_min_ms": r["causal_min_ms"],
         "fwd_tflops": fwd_tflops,
         "fwd_pct_bf16_peak": 100.0 * fwd_tflops / PEAK_BF16_TFLOPS,
         "step_pct_bf16_peak": 100.0 * (F / step_ms / 1e9) / PEAK_BF16_TFLOPS,
