@@ -257,7 +257,9 @@ def cpu_baseline(cfg, d_in, budget_s=15.0, seed=0):
     return {"value": tflops, "unit": "TFLOP/s", "cores": cores,
             "threads": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} random (b,h,t) rows of the same workload, fp64, {dt:.1f} s; "
-                      f"full workload extrapolated to {full_s:.0f} s"}
+                      f"full workload extrapolated to {full_s:.0f} s",
+            "rows": n, "seconds": dt, "rows_per_s": n / dt,
+            "full_workload_s_extrapolated": full_s}
 
 
 def decode_inputs(cfg, d_in):
@@ -790,6 +792,9 @@ def main():
     }
     if "cpu_baseline" in r:
         line["cpu_baseline"] = r["cpu_baseline"]
+        # the forward's speedup over the oracle's extrapolated full-workload time
+        line["cpu_baseline"]["gpu_fwd_speedup"] = (
+            r["cpu_baseline"]["full_workload_s_extrapolated"] * 1e3 / r["fwd_ms"])
     print(json.dumps(line), flush=True)
 
 
