@@ -15,7 +15,9 @@
 //                      through LDS and the workgroup leaves one partial state
 //                      (unnormalised O, reference max, weight sum) per row.
 //   moda_decode_merge  merges the partial states of each query row and
-//                      normalises once.
+//                      normalises once.  With one part per (b, kv head) (large
+//                      batches, short caches) the part kernel normalises and
+//                      writes the result itself and the merge is not launched.
 // Per block: K rows straight into MFMA operand registers (16 bytes of a row
 // per lane, the next block's already in flight), V rows into the wave's
 // 8 KiB of LDS, column-swizzled, read transposed; S^T = K Q^T and
@@ -195,6 +197,27 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
 
   // wave 0 writes the workgroup's state of each row: O (unnormalised), max, sum
   if (wave == 0 && row_ok) {
+    float l_row = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) l_row += l_s[w][li];
+    if (p.nsplit == 1) {
+      // the only part: normalise once and write O and LSE here, exactly as the
+      // merge would from this one state (no merge launch follows)
+      const float inv = m_row == -INFINITY ? 0.f : 1.0f / l_row;
+      __bf16 *const o = (__bf16 *)p.out + qrow * DEC_D;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 w;
+          w[0] = cvt_bf16x2(st.acc[nb][4 * q4] * inv, st.acc[nb][4 * q4 + 1] * inv);
+          w[1] = cvt_bf16x2(st.acc[nb][4 * q4 + 2] * inv, st.acc[nb][4 * q4 + 3] * inv);
+          *(u32x2 *)(o + 32 * nb + 8 * q4 + 4 * lh) = w;
+        }
+      if (p.lse && lh == 0)
+        p.lse[qrow] = m_row == -INFINITY ? -INFINITY : (m_row + __log2f(l_row)) * 0.69314718055994531f;
+      return;
+    }
     float *rec = p.ws + (qrow * p.nsplit + part) * kDecodeRecord;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -204,9 +227,6 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
             make_float4(st.acc[nb][4 * q4], st.acc[nb][4 * q4 + 1], st.acc[nb][4 * q4 + 2],
                         st.acc[nb][4 * q4 + 3]);
     if (lh == 0) {
-      float l_row = 0.f;
-#pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) l_row += l_s[w][li];
       rec[DEC_D] = m_row;
       rec[DEC_D + 1] = l_row;
     }
@@ -309,8 +329,10 @@ hipError_t launch_decode(const DecArgs &a, hipStream_t s) {
   const int64_t BH = a.B * a.Hkv;
   hipLaunchKernelGGL(moda_decode_part, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * DEC_WAVES), 0,
                      s, a);
-  hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,
-                     s, a);
+  // with one part per (b, kv head) the part kernel writes the result itself
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,
+                       s, a);
   return hipGetLastError();
 }
 
