@@ -369,8 +369,8 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char a_q1[BTILE];
   __shared__ __attribute__((aligned(16))) float lse_s[2][QROWS];  // -lse * log2(e)
   __shared__ __attribute__((aligned(16))) float del_s[2][QROWS];  // -D
-  // P of the tile as the dV wave's bf16 B operands: [group][block][k-step][lane]
-  __shared__ __attribute__((aligned(16))) bf16x8 p_x[KV_GROUPS][2][2][64];
+  // P of the tile in fp32, in the dV wave's register order: [group][block][4 rows][lane]
+  __shared__ __attribute__((aligned(16))) float4 p_x[KV_GROUPS][2][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -537,6 +537,8 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
           x[sb][4 * g + 1] = fast_exp2(fmaf(c, x[sb][4 * g + 1], l4.y));
           x[sb][4 * g + 2] = fast_exp2(fmaf(c, x[sb][4 * g + 2], l4.z));
           x[sb][4 * g + 3] = fast_exp2(fmaf(c, x[sb][4 * g + 3], l4.w));
+          p_x[kg][sb][g][lane] = float4{x[sb][4 * g], x[sb][4 * g + 1], x[sb][4 * g + 2],
+                                        x[sb][4 * g + 3]};
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -545,7 +547,6 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
           for (int q = 0; q < 4; ++q)
             u[q] = cvt_bf16x2(x[sb][8 * kk + 2 * q], x[sb][8 * kk + 2 * q + 1]);
           wb[sb][kk] = __builtin_bit_cast(bf16x8, u);
-          p_x[kg][sb][kk][lane] = wb[sb][kk];
         }
       }
     }
@@ -557,14 +558,13 @@ __global__ __launch_bounds__(64 * KV_WAVES, 1) void moda_bwd_dkdv(BwdArgs p) {
         const floatx16 &d = x[sb];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 pw = __builtin_bit_cast(u32x4, p_x[kg][sb][kk][lane]);
+          const float4 p0 = p_x[kg][sb][2 * kk][lane], p1 = p_x[kg][sb][2 * kk + 1][lane];
+          const int rr = 8 * kk;
           u32x4 u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rr = 8 * kk + 2 * q;
-            u[q] = cvt_bf16x2(bf16_bits_to_float(pw[q] & 0xFFFFu) * d[rr],
-                              bf16_bits_to_float(pw[q] >> 16) * d[rr + 1]);
-          }
+          u[0] = cvt_bf16x2(p0.x * d[rr + 0], p0.y * d[rr + 1]);
+          u[1] = cvt_bf16x2(p0.z * d[rr + 2], p0.w * d[rr + 3]);
+          u[2] = cvt_bf16x2(p1.x * d[rr + 4], p1.y * d[rr + 5]);
+          u[3] = cvt_bf16x2(p1.z * d[rr + 6], p1.w * d[rr + 7]);
           wb[sb][kk] = __builtin_bit_cast(bf16x8, u);
         }
       }
