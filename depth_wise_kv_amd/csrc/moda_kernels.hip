@@ -9,11 +9,12 @@
 // "Hardware-efficient implementation").
 //
 // Kernels:
-//   moda_fwd_mfma   bf16, d = 128.  A workgroup owns 256 query rows made of
-//                   256/G tokens x the G heads of one KV group, so one K/V
-//                   tile in LDS and one depth span serve all G heads (the
-//                   group-aware indexing of the same section).  QK^T and PV
-//                   run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//   moda_fwd_mfma   bf16, d = 128.  A workgroup owns 256 query rows (128 on
+//                   grids too small to fill the chip) made of rows/G tokens x
+//                   the G heads of one KV group, so one K/V tile in LDS and
+//                   one depth span serve all G heads (the group-aware indexing
+//                   of the same section).  QK^T and PV run on
+//                   v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //   moda_pack_mfma  repacks [B,Hkv,T,L,d] depth K/V into blocks of 8 tokens x
 //                   4 entries laid out in MFMA operand order, K half then V
 //                   half, so each wave streams its depth span with fully
