@@ -643,8 +643,8 @@ def main():
                     help="copy a 1 GiB buffer (steps times): HBM counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); sharding over "
+              "several GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     from synth import WORKLOADS, sweep_points
