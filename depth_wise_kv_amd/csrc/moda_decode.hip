@@ -174,23 +174,30 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] *= alpha;
-  float *const red = (float *)&slots[0][0];  // 4 regions of 64 registers x 64 lanes
+  // Only the lanes of the G real rows carry data; they move their 64
+  // accumulators as 16 float4s per step (16 KiB regions, a lane's float4 i at
+  // 64*i + lane, so a wave's store covers 1 KiB of consecutive banks).
+  float4 *const red = (float4 *)&slots[0][0];
 #pragma unroll
   for (int step = DEC_WAVES / 2; step >= 1; step >>= 1) {
-    if (wave >= step && wave < 2 * step) {
-      float *r = red + (wave - step) * 4096 + lane;
+    if (wave >= step && wave < 2 * step && row_ok) {
+      float4 *r = red + (wave - step) * 1024 + lane;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) r[(16 * nb + rr) * 64] = st.acc[nb][rr];
+      for (int i = 0; i < 16; ++i)
+        r[64 * i] = make_float4(st.acc[i >> 2][4 * (i & 3)], st.acc[i >> 2][4 * (i & 3) + 1],
+                                st.acc[i >> 2][4 * (i & 3) + 2], st.acc[i >> 2][4 * (i & 3) + 3]);
     }
     __syncthreads();
-    if (wave < step) {
-      const float *r = red + wave * 4096 + lane;
+    if (wave < step && row_ok) {
+      const float4 *r = red + wave * 1024 + lane;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) st.acc[nb][rr] += r[(16 * nb + rr) * 64];
+      for (int i = 0; i < 16; ++i) {
+        const float4 x = r[64 * i];
+        st.acc[i >> 2][4 * (i & 3)] += x.x;
+        st.acc[i >> 2][4 * (i & 3) + 1] += x.y;
+        st.acc[i >> 2][4 * (i & 3) + 2] += x.z;
+        st.acc[i >> 2][4 * (i & 3) + 3] += x.w;
+      }
     }
     __syncthreads();
   }
