@@ -199,4 +199,41 @@ __device__ __forceinline__ void softmax_update_eager(MfmaState &st, const floatx
   st.lsum += tile_weights<NB>(s, scale_log2, m_new == -INFINITY ? 0.f : -m_new, pb);
 }
 
+// softmax_update_eager<1> for a block in which a row holds at most two
+// entries: its scores sa and sb (-inf where absent) sit in registers pos and
+// pos + 8 of its 16, and the other 14 are masked (pos < 0: none).  The result
+// is bit for bit that of softmax_update_eager<1> on the masked block (the same
+// reference max, weights, sum and bf16 operands, zeros elsewhere), without the
+// 14 exponentials of zero weights.
+__device__ __forceinline__ void softmax_update_pair(MfmaState &st, float sa, float sb, int pos,
+                                                    float scale_log2, bf16x8 *pb) {
+  const float m_new = fmaxf(pair_max(fmaxf(sa, sb)) * scale_log2, st.m);
+  if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+    const float alpha = m_new == st.m ? 1.0f : fast_exp2(st.m - m_new);  // 0 from -inf
+    st.lsum *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[nb][r] *= alpha;
+  }
+  st.m = m_new;
+  // a row that has seen no unmasked entry yet keeps m = -inf and weight 0
+  const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+  const float wa = fast_exp2(fmaf(sa, scale_log2, neg_m));
+  const float wb = fast_exp2(fmaf(sb, scale_log2, neg_m));
+  st.lsum += wa + wb;
+  // register pos of each 8-register half: half (pos & 1) of 32-bit word pos / 2
+  const int sh = 16 * (pos & 1);
+  const uint32_t ba = cvt_bf16x2(wa, 0.f) << sh, bb = cvt_bf16x2(wb, 0.f) << sh;
+  u32x4 w0, w1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool here = (pos >> 1) == q;
+    w0[q] = here ? ba : 0u;
+    w1[q] = here ? bb : 0u;
+  }
+  pb[0] = __builtin_bit_cast(bf16x8, w0);
+  pb[1] = __builtin_bit_cast(bf16x8, w1);
+}
+
 }  // namespace moda

@@ -340,17 +340,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
             for (int ks = 0; ks < 8; ++ks)
               kd[ks] = *(const u32x4 *)(kp + KSTEP * kPackedBlockBytes + ks * 1024);
           }
-          // register rr holds block row 8*(rr/4) + 4*lh + rr%4: token
-          // (rr%4) | ((rr/4)%2) << 2 of the group and entry 4*eg + 2*(rr/8) + lh;
-          // keep it iff that is this row's token and an entry below L (a row of
-          // another group, or an idle row, keeps none)
+          // register rr holds block row 8*(rr/4) + 4*lh + rr%4: token rr%8 of
+          // the group and entry 4*eg + 2*(rr/8) + lh.  Of a row's 16 scores only
+          // registers tpos and tpos + 8 (its own token tpos; entries ebase and
+          // ebase + 2) can count, and each only for an entry below L; a row of
+          // another group, or an idle row, keeps none.
           const int64_t tpos64 = tok - kGroupTokens * tg;
           const int tpos = (int)(tpos64 < 0 || tpos64 >= kGroupTokens ? -1 : tpos64);
           const int64_t ebase = kGroupEntries * eg + lh;
+          float sa = sd[0][0], sb = sd[0][8];
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if (tpos != tok_of_row(8 * (rr >> 2) + (rr & 3)) || ebase + 2 * (rr >> 3) >= L)
-              sd[0][rr] = -INFINITY;
+          for (int r = 1; r < kGroupTokens; ++r) {
+            sa = tpos == r ? sd[0][r] : sa;
+            sb = tpos == r ? sd[0][r + 8] : sb;
+          }
+          sa = tpos >= 0 && ebase < L ? sa : -INFINITY;
+          sb = tpos >= 0 && ebase + 2 < L ? sb : -INFINITY;
           eg += KSTEP;
           while (eg >= ne) {
             eg -= ne;
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void moda_fwd_mfma(FwdArgs p) {
           // a row's L entries span ceil(L/4) blocks: take each block's max, so
           // that a dominant entry in a later block still gets weight 1 exactly
           bf16x8 pb[2];
-          softmax_update_eager<1>(st, sd, p.scale_log2, pb);
+          softmax_update_pair(st, sa, sb, tpos, p.scale_log2, pb);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
