@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "moda_device.h"
 #include "moda_internal.h"
@@ -96,15 +97,17 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) st.acc[nb4][rr] = 0.f;
 
-  // K rows of block j as MFMA A operands: entry 32*j' + li of its source, dims 64*lh + 8*ks
+  // K rows of block j as MFMA A operands: entry 32*j' + li of its source, dims
+  // 64*lh + 8*ks.  A row past the source's last entry reads that entry instead
+  // (its scores are masked below); the loads carry no per-lane condition, which
+  // would put branches around them and make the compiler wait for them early.
   auto load_k = [&](int64_t j, u32x4 (&kd)[8]) {
     const bool dep = j >= nbc;
     const int64_t e = (dep ? j - nbc : j) * 32 + li;
-    const int64_t n = dep ? p.L : n_c;
-    const __bf16 *src = (dep ? kdp : kc) + e * DEC_D + 64 * lh;
+    const int64_t n = dep ? p.L : n_c;  // >= 1 for every block visited
+    const __bf16 *src = (dep ? kdp : kc) + (e < n ? e : n - 1) * DEC_D + 64 * lh;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kd[ks] = e < n ? *(const u32x4 *)(src + 8 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < 8; ++ks) kd[ks] = *(const u32x4 *)(src + 8 * ks);
   };
   // this wave's blocks: every DEC_WAVES-th from j_lo + wave, stepping over the
   // empty cache blocks, so that every block visited has an entry in lane 0
@@ -112,10 +115,13 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
     return (j >= jc_end && j < nbc) ? j + (nbc - j + DEC_WAVES - 1) / DEC_WAVES * DEC_WAVES : j;
   };
   u32x4 kd[8];
-  const int64_t j_first = skip_empty(j_lo + wave);
-  if (j_first < j_hi) load_k(j_first, kd);
-  for (int64_t j = j_first, jn; j < j_hi; j = jn) {
-    jn = skip_empty(j + DEC_WAVES);
+  // One block: its V rows into the slot, S^T on the K rows in kd, then (but
+  // for the wave's last block) the next block's K rows into kd, the softmax,
+  // the PV products.  The V loads go out before the next K loads (loads
+  // complete in order), so the PV products wait for V alone; the last block is
+  // a separate copy without the K request, since behind a branch the compiler
+  // would wait for those loads too before the V reads.
+  auto block_step = [&](int64_t j, int64_t jn, auto prefetch) {
     const bool dep = j >= nbc;
     const int64_t e0 = (dep ? j - nbc : j) * 32;
     const int64_t n = dep ? p.L : n_c;
@@ -139,8 +145,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
                                                             qb[ks], sd2[ks & 1], 0, 0, 0);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) sd[0][rr] = sd2[0][rr] + sd2[1][rr];
-    const bool more = jn < j_hi;
-    if (more) load_k(jn, kd);
+    if constexpr (decltype(prefetch)::value) load_k(jn, kd);
     // register rr holds entry e0 + 8*(rr/4) + 4*lh + rr%4: entries past the source drop out
     const int64_t lim64 = n - e0 - 4 * lh;
     const int lim = (int)(lim64 > 64 ? 64 : lim64);
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
     bf16x8 pb[2];
     softmax_update<1>(st, sd, p.scale_log2, pb);
     // the V rows have landed (the next block's K loads may still be in flight)
-    if (more) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    if constexpr (decltype(prefetch)::value) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
     else wait_vmem();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -158,6 +163,13 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
       for (int nb4 = 0; nb4 < 4; ++nb4)
         st.acc[nb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.colfrag(slot, 4 * nb4 + kk),
                                                               pb[kk], st.acc[nb4], 0, 0, 0);
+  };
+  int64_t j = skip_empty(j_lo + wave);
+  if (j < j_hi) {
+    load_k(j, kd);
+    for (int64_t jn = skip_empty(j + DEC_WAVES); jn < j_hi; j = jn, jn = skip_empty(j + DEC_WAVES))
+      block_step(j, jn, std::true_type{});
+    block_step(j, j, std::false_type{});
   }
 
   // Merge the 8 waves' states: a common reference max per row, then the
