@@ -189,16 +189,31 @@ moda_status check_qkvo(const void *q, const void *k, const void *v, const void *
 // Decode split: per (b, kv head) the cache's and the depth entries' 32-entry
 // blocks form one list, cut into nsplit even parts, one workgroup each.  The
 // parts fill the chip once (one 8-wave workgroup per compute unit, 256 units)
-// while every wave still gets a block.
-constexpr int64_t kDecodeGroups = 256;
-constexpr int64_t kDecodeWaves = 8;
+// while every wave still gets a block.  Where the blocks, not the chip, limit
+// that split to half the units or fewer (short caches, few heads), parts of 4
+// waves double the count: more units share the stream, and a part waits for
+// its slowest of 4 waves, not 8, before the waves merge.
+constexpr int64_t kDecodeUnits = 256;
 
-int64_t decode_splits(const moda_shape *s) {
+struct DecodePlan {
+  int64_t nsplit;
+  int waves;
+};
+
+DecodePlan decode_plan(const moda_shape *s) {
   const int64_t BH = s->B * s->Hkv;
   const int64_t nb = (s->T + 31) / 32 + (s->L + 31) / 32;
-  int64_t n = kDecodeGroups / BH;
-  if (n > nb / kDecodeWaves) n = nb / kDecodeWaves;
-  return n < 1 ? 1 : n;
+  auto splits = [&](int64_t waves) {
+    int64_t n = kDecodeUnits * (8 / waves) / BH;
+    if (n > nb / waves) n = nb / waves;
+    return n < 1 ? (int64_t)1 : n;
+  };
+  const int64_t n8 = splits(8);
+  if (BH * n8 <= kDecodeUnits / 2) {
+    const int64_t n4 = splits(4);
+    if (n4 > n8) return {n4, 4};
+  }
+  return {n8, 8};
 }
 
 moda_status check_decode_shape(const moda_shape *s) {
@@ -212,7 +227,7 @@ moda_status check_decode_shape(const moda_shape *s) {
 }
 
 size_t decode_ws_bytes(const moda_shape *s) {
-  return (size_t)(s->B * s->Hq * decode_splits(s) * moda::kDecodeRecord * 4);
+  return (size_t)(s->B * s->Hq * decode_plan(s).nsplit * moda::kDecodeRecord * 4);
 }
 
 // shape and tensor arguments of a decode call (everything but the workspace)
@@ -261,7 +276,9 @@ moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
   a.Hkv = s->Hkv;
   a.T = s->T;
   a.L = s->L;
-  a.nsplit = decode_splits(s);
+  const DecodePlan plan = decode_plan(s);
+  a.nsplit = plan.nsplit;
+  a.waves = plan.waves;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s->d));
   return hip_status(moda::launch_decode(a, (hipStream_t)hip_stream), "decode launch");
 }

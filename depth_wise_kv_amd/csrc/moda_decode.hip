@@ -10,10 +10,12 @@
 //   moda_decode_part   a workgroup takes one part of one (b, kv head)'s
 //                      entries (the cache's, then the depth entries, as one
 //                      list of 32-entry blocks split into nsplit even parts).
-//                      Each of its 8 waves walks every 8th block of the
-//                      part; the waves then merge their softmax states
-//                      through LDS and the workgroup leaves one partial state
-//                      (unnormalised O, reference max, weight sum) per row.
+//                      Each of its W waves (8; 4 where short caches leave
+//                      most of the chip idle otherwise) walks every W-th
+//                      block of the part; the waves then merge their softmax
+//                      states through LDS and the workgroup leaves one partial
+//                      state (unnormalised O, reference max, weight sum) per
+//                      row.
 //   moda_decode_merge  merges the partial states of each query row and
 //                      normalises once.  With one part per (b, kv head) (large
 //                      batches, short caches) the part kernel normalises and
@@ -33,11 +35,11 @@
 
 namespace moda {
 
-constexpr int DEC_WAVES = 8;
 constexpr int DEC_D = kMfmaD;  // 128
 constexpr int MERGE_WAVES = 16;
 constexpr int MERGE_UNROLL = 8;
 
+template <int DEC_WAVES>
 __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
   __shared__ __attribute__((aligned(1024))) char slots[DEC_WAVES][32 * 256];
   __shared__ float m_s[DEC_WAVES][32], l_s[DEC_WAVES][32];
@@ -346,8 +348,10 @@ hipError_t decode_scratch(void **ptr) {
 
 hipError_t launch_decode(const DecArgs &a, hipStream_t s) {
   const int64_t BH = a.B * a.Hkv;
-  hipLaunchKernelGGL(moda_decode_part, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * DEC_WAVES), 0,
-                     s, a);
+  if (a.waves == 4)
+    hipLaunchKernelGGL(moda_decode_part<4>, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * 4), 0, s, a);
+  else
+    hipLaunchKernelGGL(moda_decode_part<8>, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * 8), 0, s, a);
   // with one part per (b, kv head) the part kernel writes the result itself
   if (a.nsplit > 1)
     hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,

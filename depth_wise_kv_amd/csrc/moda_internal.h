@@ -71,6 +71,7 @@ struct DecArgs {
   float *ws;                        // [B*Hq, nsplit, kDecodeRecord]
   int64_t B, Hq, Hkv, T, L;
   int64_t nsplit;
+  int waves;         // waves per part workgroup: 4 or 8
   float scale_log2;  // log2(e) / sqrt(d)
 };
 

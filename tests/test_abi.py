@@ -126,11 +126,16 @@ def test_decode_workspace_and_rejects(m):
     s = shape(m, T=65536, L=32)
     ws = m.moda_decode_workspace_bytes(s)
     rec = 132 * 4  # one record (O, max, sum, padding) per query row and workgroup part
-    # parts per (b, kv head): 256 workgroups in all, but at least 8 blocks of 32 entries each
+    # parts per (b, kv head): 256 8-wave workgroups in all, but at least 8 blocks of 32
+    # entries each; where that fills at most 128 units, 4-wave parts of at least 4 blocks
+    # each, up to 512
     assert ws == 16 * 64 * rec
     assert m.moda_decode_workspace_bytes(shape(m, T=65536, L=0)) == 16 * 64 * rec
-    assert m.moda_decode_workspace_bytes(shape(m, T=4096, L=24)) == 16 * 16 * rec
+    # 129 blocks: 16 8-wave parts (64 workgroups), so 32 4-wave parts
+    assert m.moda_decode_workspace_bytes(shape(m, T=4096, L=24)) == 16 * 32 * rec
     assert m.moda_decode_workspace_bytes(shape(m, B=64, T=4096)) == 64 * 16 * 1 * rec
+    # 13 blocks per (b, kv head), 48 KV heads in all: 1 8-wave part (48 workgroups), so 3 4-wave parts
+    assert m.moda_decode_workspace_bytes(shape(m, B=12, T=384)) == 12 * 16 * 3 * rec
     assert m.moda_decode_workspace_bytes(shape(m, T=1, L=0)) == 16 * 1 * rec
     s0 = shape(m, T=65536, L=0)
     assert m.moda_decode_workspace_bytes(shape(m, dtype="f32")) == 0
