@@ -254,23 +254,28 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void moda_decode_part(DecArgs p) {
   }
 }
 
-// One workgroup per query row: each wave folds every 16th partial state into
-// a running (max, sum, O), the 16 wave states merge in LDS, one normalisation.
-__global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p) {
-  __shared__ float o_s[MERGE_WAVES][DEC_D];
-  __shared__ float m_s[MERGE_WAVES], l_s[MERGE_WAVES];
+// One workgroup per query row, of NW waves (one per MERGE_UNROLL records, a
+// power of two up to MERGE_WAVES): each wave folds every NW-th partial state
+// into a running (max, sum, O), its loads in flight together; the NW wave
+// states merge in LDS, one normalisation.  NW depends on nsplit alone, so the
+// order of the sums is fixed by the shape.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void moda_decode_merge(DecArgs p) {
+  __shared__ float o_s[NW][DEC_D];
+  __shared__ float m_s[NW], l_s[NW];
   const int64_t row = blockIdx.x;  // b * Hq + head
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  constexpr int nw = NW;
   const int64_t n = p.nsplit;
   const float *rec = p.ws + row * n * kDecodeRecord;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int64_t base = wave; base < n; base += MERGE_WAVES * MERGE_UNROLL) {
+  for (int64_t base = wave; base < n; base += (int64_t)nw * MERGE_UNROLL) {
     float mi[MERGE_UNROLL], li[MERGE_UNROLL];
     float2 oi[MERGE_UNROLL];
 #pragma unroll
     for (int u = 0; u < MERGE_UNROLL; ++u) {
-      const int64_t idx = base + MERGE_WAVES * u;
+      const int64_t idx = base + (int64_t)nw * u;
       const float *r = rec + (idx < n ? idx : 0) * kDecodeRecord;
       mi[u] = idx < n ? r[DEC_D] : -INFINITY;
       li[u] = r[DEC_D + 1];
@@ -298,10 +303,10 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void moda_decode_merge(DecArgs p)
   if (wave != 0) return;
   float M = m_s[0];
 #pragma unroll
-  for (int w = 1; w < MERGE_WAVES; ++w) M = fmaxf(M, m_s[w]);
+  for (int w = 1; w < nw; ++w) M = fmaxf(M, m_s[w]);
   float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
-  for (int w = 0; w < MERGE_WAVES; ++w) {
+  for (int w = 0; w < nw; ++w) {
     if (m_s[w] == -INFINITY) continue;
     const float c = fast_exp2(m_s[w] - M);
     L += l_s[w] * c;
@@ -353,9 +358,19 @@ hipError_t launch_decode(const DecArgs &a, hipStream_t s) {
   else
     hipLaunchKernelGGL(moda_decode_part<8>, dim3((uint32_t)(BH * a.nsplit)), dim3(64 * 8), 0, s, a);
   // with one part per (b, kv head) the part kernel writes the result itself
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL(moda_decode_merge, dim3((uint32_t)(a.B * a.Hq)), dim3(64 * MERGE_WAVES), 0,
-                       s, a);
+  if (a.nsplit > 1) {
+    // one merge wave per MERGE_UNROLL records, a power of two up to MERGE_WAVES
+    int nw = 1;
+    while (nw < MERGE_WAVES && (int64_t)nw * MERGE_UNROLL < a.nsplit) nw *= 2;
+    const dim3 grid((uint32_t)(a.B * a.Hq));
+    switch (nw) {
+      case 1: hipLaunchKernelGGL(moda_decode_merge<1>, grid, dim3(64), 0, s, a); break;
+      case 2: hipLaunchKernelGGL(moda_decode_merge<2>, grid, dim3(128), 0, s, a); break;
+      case 4: hipLaunchKernelGGL(moda_decode_merge<4>, grid, dim3(256), 0, s, a); break;
+      case 8: hipLaunchKernelGGL(moda_decode_merge<8>, grid, dim3(512), 0, s, a); break;
+      default: hipLaunchKernelGGL(moda_decode_merge<16>, grid, dim3(1024), 0, s, a); break;
+    }
+  }
   return hipGetLastError();
 }
 
