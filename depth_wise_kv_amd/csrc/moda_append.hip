@@ -10,11 +10,12 @@
 //                        (blocks of 8 tokens x 4 entries; K half in MFMA
 //                        A-operand order, V half with each 16-byte chunk
 //                        holding one entry's dim for the group's 8 tokens).
-//                        One workgroup per (kv head, token group, new entry):
+//                        One workgroup per (kv head, token group, entry pair
+//                        touched), writing the pair's new entries in turn:
 //                        the 8 tokens' new K rows go into the K half as 16-byte
-//                        chunks in 64-byte runs, and their V rows, regrouped
-//                        through LDS by dim, fill whole V chunks, four
-//                        contiguous 512-byte runs.
+//                        chunks in 64-byte runs (two entries fill a 128-byte
+//                        line), and their V rows, regrouped through LDS by dim,
+//                        fill whole V chunks, four contiguous 512-byte runs.
 //   moda_append_generic  the generic layout (natural Kd, then natural Vd):
 //                        one thread per 16 bytes, a strided copy.
 #include <hip/hip_runtime.h>
@@ -29,14 +30,18 @@ constexpr int AP_D = kMfmaD;                     // 128
 constexpr int AP_HALF = kDepthBlock * AP_D * 2;  // bytes of a block's K half
 
 __global__ __launch_bounds__(256) void moda_append_mfma(AppendArgs p) {
-  // grid: x = token group, y = kv head (b * Hkv + g), z = new entry el < n
+  // grid: x = token group, y = kv head (b * Hkv + g), z = the entry pairs
+  // (2k, 2k + 1) that [first, first + n) touches, in order.  A workgroup writes
+  // the new entries of its pair, one after the other: the two share the K
+  // half's 128-byte lines (64 bytes each), which then fill in one L2 instead
+  // of leaving two L2s as two partial writes.
   __shared__ __attribute__((aligned(16))) uint16_t v_s[kGroupTokens][AP_D + 8];
   const int tid = threadIdx.x;
-  const int64_t tg = blockIdx.x, bh = blockIdx.y, el = blockIdx.z;
-  const int64_t e = p.first + el;  // the entry this workgroup writes
-  const int64_t eg = e / kGroupEntries;
-  const int eo = (int)(e - kGroupEntries * eg);  // entry within the entry group
-  const int kk = eo >> 1, h = eo & 1;            // block rows 16kk + 8a + 4h + b hold it
+  const int64_t tg = blockIdx.x, bh = blockIdx.y;
+  const int64_t pr = p.first / 2 + blockIdx.z;  // the pair: entries 2pr, 2pr + 1
+  const int64_t e_lo = 2 * pr > p.first ? 2 * pr : p.first;
+  const int64_t e_end = p.first + p.n, e_hi = 2 * pr + 2 < e_end ? 2 * pr + 2 : e_end;
+  const int64_t eg = pr / 2;  // its entry group
   const int64_t ne = (p.L + kGroupEntries - 1) / kGroupEntries;
   char *const blk = (char *)p.packed + (bh * p.nblk + tg * ne + eg) * kPackedBlockBytes;
   // thread (token j = tid / 16 % 8, 16-byte column c16 = tid % 16); threads 128..255
@@ -44,29 +49,35 @@ __global__ __launch_bounds__(256) void moda_append_mfma(AppendArgs p) {
   const int j = (tid >> 4) & 7, c16 = tid & 15;
   const int64_t t = kGroupTokens * tg + j;
   const bool valid = t < p.T;
-  const int64_t src = ((bh * p.T + (valid ? t : 0)) * p.n + el) * AP_D + 8 * c16;
-  if (tid < 128) {
-    // K row of token j: dims 8*c16 .. +7 go to k-step c16 % 8, lane r + 32 * (c16 / 8)
-    // of block row r = 16kk + 8(j/4) + 4h + j%4
-    if (valid) {
-      const u32x4 kv = *(const u32x4 *)((const __bf16 *)p.knew + src);
-      const int r = 16 * kk + 8 * (j >> 2) + 4 * h + (j & 3);
-      *(u32x4 *)(blk + ((c16 & 7) * 64 + r + 32 * (c16 >> 3)) * 16) = kv;
+  for (int64_t e = e_lo; e < e_hi; ++e) {
+    const int64_t el = e - p.first;  // the entry's index among the new ones
+    const int eo = (int)(e - kGroupEntries * eg);  // entry within the entry group
+    const int kk = eo >> 1, h = eo & 1;            // block rows 16kk + 8a + 4h + b hold it
+    const int64_t src = ((bh * p.T + (valid ? t : 0)) * p.n + el) * AP_D + 8 * c16;
+    if (tid < 128) {
+      // K row of token j: dims 8*c16 .. +7 go to k-step c16 % 8, lane r + 32 * (c16 / 8)
+      // of block row r = 16kk + 8(j/4) + 4h + j%4
+      if (valid) {
+        const u32x4 kv = *(const u32x4 *)((const __bf16 *)p.knew + src);
+        const int r = 16 * kk + 8 * (j >> 2) + 4 * h + (j & 3);
+        *(u32x4 *)(blk + ((c16 & 7) * 64 + r + 32 * (c16 >> 3)) * 16) = kv;
+      }
+    } else {
+      const u32x4 vv = valid ? *(const u32x4 *)((const __bf16 *)p.vnew + src) : u32x4{0, 0, 0, 0};
+      *(u32x4 *)&v_s[j][8 * c16] = vv;
     }
-  } else {
-    const u32x4 vv = valid ? *(const u32x4 *)((const __bf16 *)p.vnew + src) : u32x4{0, 0, 0, 0};
-    *(u32x4 *)&v_s[j][8 * c16] = vv;
-  }
-  __syncthreads();
-  if (tid >= 128) {
-    // V chunk (nb, kk, lane 32h + dl): dim 32nb + dl of the 8 tokens, token j at element j
-    const int u = tid - 128, nb = u >> 5, dl = u & 31, dim = 32 * nb + dl;
-    u32x4 w;
+    __syncthreads();
+    if (tid >= 128) {
+      // V chunk (nb, kk, lane 32h + dl): dim 32nb + dl of the 8 tokens, token j at element j
+      const int u = tid - 128, nb = u >> 5, dl = u & 31, dim = 32 * nb + dl;
+      u32x4 w;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)v_s[2 * q][dim] | ((uint32_t)v_s[2 * q + 1][dim] << 16);
-    // tokens past T: their elements are zero (the loads above read zeros for them)
-    *(u32x4 *)(blk + AP_HALF + ((2 * nb + kk) * 64 + 32 * h + dl) * 16) = w;
+      for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)v_s[2 * q][dim] | ((uint32_t)v_s[2 * q + 1][dim] << 16);
+      // tokens past T: their elements are zero (the loads above read zeros for them)
+      *(u32x4 *)(blk + AP_HALF + ((2 * nb + kk) * 64 + 32 * h + dl) * 16) = w;
+    }
+    __syncthreads();  // v_s is refilled for the next entry
   }
 }
 
@@ -87,8 +98,10 @@ __global__ __launch_bounds__(256) void moda_append_generic(AppendArgs p, int row
 
 hipError_t launch_append(const AppendArgs &a, bool mfma, int row_bytes, hipStream_t s) {
   if (mfma) {
+    // the entry pairs (2k, 2k + 1) that [first, first + n) touches
+    const int64_t pairs = (a.first + a.n - 1) / 2 - a.first / 2 + 1;
     const dim3 grid((uint32_t)((a.T + kGroupTokens - 1) / kGroupTokens), (uint32_t)(a.B * a.Hkv),
-                    (uint32_t)a.n);
+                    (uint32_t)pairs);
     hipLaunchKernelGGL(moda_append_mfma, grid, dim3(256), 0, s, a);
   } else {
     const int row16 = row_bytes / 16;
