@@ -10,14 +10,14 @@
 //   moda_decode_part   a workgroup takes one part of one (b, kv head)'s
 //                      entries (the cache's, then the depth entries, as one
 //                      list of 32-entry blocks split into nsplit even parts).
-//                      Each of its W waves (8; 4 where short caches leave
-//                      most of the chip idle otherwise) walks every W-th
+//                      Each of its W waves (8; 4 where 8-wave parts would
+//                      leave half the chip or more idle) walks every W-th
 //                      block of the part; the waves then merge their softmax
 //                      states through LDS and the workgroup leaves one partial
 //                      state (unnormalised O, reference max, weight sum) per
 //                      row.
-//   moda_decode_merge  merges the partial states of each query row and
-//                      normalises once.  With one part per (b, kv head) (large
+//   moda_decode_merge  merges the partial states of each query row (one wave
+//                      per 8 of them, up to 16) and normalises once.  With one part per (b, kv head) (large
 //                      batches, short caches) the part kernel normalises and
 //                      writes the result itself and the merge is not launched.
 // Per block: K rows straight into MFMA operand registers (16 bytes of a row
