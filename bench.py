@@ -208,6 +208,41 @@ def timed(fn, steps, stream, graph=True, flush=None):
     return pairs(max(steps, 20), fn)
 
 
+def finished_points(path):
+    """Names of the sweep points whose lines a results file already holds
+    (none if there is no file); a truncated last line counts as unfinished."""
+    done = set()
+    if not path or not os.path.exists(path):
+        return done
+    with open(path) as f:
+        for line in f:
+            try:
+                rec = json.loads(line)
+            except json.JSONDecodeError:
+                continue
+            if isinstance(rec, dict) and "config" in rec:
+                done.add(rec["config"])
+    return done
+
+
+def emit_point(path, rec):
+    """Print a sweep point's JSON line and, with a results file, append it
+    there as one write followed by a flush to disk."""
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if path:
+        # a run killed mid-write may have left a last line without its newline
+        torn = False
+        if os.path.exists(path) and os.path.getsize(path) > 0:
+            with open(path, "rb") as f:
+                f.seek(-1, os.SEEK_END)
+                torn = f.read(1) != b"\n"
+        with open(path, "a") as f:
+            f.write(("\n" if torn else "") + line + "\n")
+            f.flush()
+            os.fsync(f.fileno())
+
+
 def center(t, cold):
     """The duration a timing reports: the mean of warm samples (the average
     launch duration), the median of cold ones (a rare call after the cache
@@ -634,6 +669,10 @@ def main():
                     help="time the decode step on the decode shapes (one JSON line each)")
     ap.add_argument("--only", default=None,
                     help="with --sweep: run only points whose name contains this string")
+    ap.add_argument("--results", default=None,
+                    help="with --sweep: also append each finished point's JSON line to this "
+                         "file, and skip the points it already holds (an interrupted sweep "
+                         "resumes where it stopped)")
     ap.add_argument("--profile-kernel", choices=["fwd", "causal", "pack", "depth", "bwd", "decode", "append"],
                     help="only launch this kernel (steps times) for counter collection")
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
@@ -704,12 +743,17 @@ def main():
         stack_run(dict(named[args.config]), args.steps)
         return
     if args.sweep:
+        done = finished_points(args.results)
         for c in sweep_points():
             if args.only and args.only not in c["name"]:
                 continue
+            if c["name"] in done:
+                print(f"bench.py: {c['name']} already in {args.results}; skipped",
+                      file=sys.stderr, flush=True)
+                continue
             r = bench_config(c, args.steps, args.warmup, False, causal=True,
                              with_bwd=args.sweep_bwd, ablation=args.ablation)
-            print(json.dumps({"config": c["name"], "T": c["T"], "L": c["L"],
+            emit_point(args.results, {"config": c["name"], "T": c["T"], "L": c["L"],
                               "G": c["Hq"] // c["Hkv"], "fwd_ms": r["fwd_ms"],
                               "fwd_warm_cache_ms": r["fwd_warm_ms"],
                               "kernel_timing_cache": r["cache"],
@@ -730,7 +774,7 @@ def main():
                                                  if r["decode_ms"] else None),
                               "bwd_ms": r["bwd_ms"],
                               "bwd_tflops": (2.5 * flops(c) / r["bwd_ms"] / 1e9
-                                             if r["bwd_ms"] else None)}), flush=True)
+                                             if r["bwd_ms"] else None)})
         return
 
     cfg = dict(named[args.config])

@@ -27,6 +27,25 @@ moda_status ok() {
   return MODA_OK;
 }
 
+// MODA_LOG=1 (any value but "0") makes every call that enqueues work print one
+// line to stderr when it returns: the entry point, the shape, the kernel the
+// shape selects, and "ok" or the error.  The calls' own error texts are what
+// moda_last_error() returns.
+bool log_enabled() {
+  static const bool on = [] {
+    const char *e = std::getenv("MODA_LOG");
+    return e && *e && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+struct CallLog {
+  const char *name;
+  const moda_shape *s;
+  CallLog(const char *n, const moda_shape *sh) : name(n), s(sh) { g_last_error.clear(); }
+  ~CallLog();
+};
+
 constexpr int64_t kMaxElems = (int64_t)1 << 62;
 
 // a * b * ... without overflow past kMaxElems; returns -1 on overflow
@@ -285,6 +304,26 @@ moda_status decode_impl(const moda_shape *s, const int32_t *lens, const void *q,
 
 }  // namespace
 
+namespace {
+CallLog::~CallLog() {
+  if (!log_enabled()) return;
+  // the variant lookup validates the shape again, which sets or clears the
+  // thread's last error: keep the call's own
+  const std::string err = g_last_error;
+  const char *result = err.empty() ? "ok" : err.c_str();
+  if (!s) {
+    std::fprintf(stderr, "moda: %s (no shape): %s\n", name, result);
+    return;
+  }
+  const std::string variant = moda_fwd_variant(s);
+  g_last_error = err;
+  std::fprintf(stderr, "moda: %s B=%lld Hq=%lld Hkv=%lld T=%lld L=%lld d=%lld %s [%s]: %s\n",
+               name, (long long)s->B, (long long)s->Hq, (long long)s->Hkv, (long long)s->T,
+               (long long)s->L, (long long)s->d, s->dtype == MODA_BF16 ? "bf16" : "f32",
+               variant.c_str(), result);
+}
+}  // namespace
+
 extern "C" {
 
 moda_status moda_check_shape(const moda_shape *s) {
@@ -314,6 +353,7 @@ const char *moda_fwd_variant(const moda_shape *s) {
 
 moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth, const void *v_depth,
                                   void *packed, size_t packed_bytes, void *hip_stream) {
+  CallLog log_("moda_pack_depth_cache", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_pack_depth_cache needs L >= 1");
@@ -334,6 +374,7 @@ moda_status moda_pack_depth_cache(const moda_shape *s, const void *k_depth, cons
 moda_status moda_append_depth(const moda_shape *s, int64_t first, int64_t n, const void *k_new,
                               const void *v_new, void *packed, size_t packed_bytes,
                               void *hip_stream) {
+  CallLog log_("moda_append_depth", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_append_depth needs L >= 1");
@@ -360,6 +401,7 @@ moda_status moda_append_depth(const moda_shape *s, int64_t first, int64_t n, con
 moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
                      const void *packed, size_t packed_bytes, void *out, float *lse,
                      void *hip_stream) {
+  CallLog log_("moda_fwd", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   st = check_qkvo(q, k, v, out, lse);
@@ -379,6 +421,7 @@ moda_status moda_fwd(const moda_shape *s, const void *q, const void *k, const vo
 
 moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, const void *v,
                             void *out, float *lse, void *hip_stream) {
+  CallLog log_("moda_causal_fwd", s);
   if (!s) return fail(MODA_ERR_INVALID_ARG, "shape is NULL");
   moda_shape s0 = *s;
   s0.L = 0;
@@ -395,6 +438,7 @@ moda_status moda_causal_fwd(const moda_shape *s, const void *q, const void *k, c
 
 moda_status moda_depth_fwd(const moda_shape *s, const void *q, const void *packed,
                            size_t packed_bytes, void *out, float *lse, void *hip_stream) {
+  CallLog log_("moda_depth_fwd", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (s->L < 1) return fail(MODA_ERR_INVALID_ARG, "moda_depth_fwd needs L >= 1");
@@ -508,6 +552,7 @@ moda_status moda_bwd(const moda_shape *s, const void *q, const void *k, const vo
                      size_t packed_bytes, const void *out, const float *lse, const void *dout,
                      void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth, float *delta,
                      void *hip_stream) {
+  CallLog log_("moda_bwd", s);
   return bwd_impl(s, q, k, v, k_depth, v_depth, packed, packed_bytes, out, lse, dout, dq, dk, dv,
                   dk_depth, dv_depth, delta, 1, nullptr, hip_stream);
 }
@@ -523,6 +568,7 @@ moda_status moda_bwd_ws(const moda_shape *s, const void *q, const void *k, const
                         void *dq, void *dk, void *dv, void *dk_depth, void *dv_depth,
                         float *delta, void *workspace, size_t workspace_bytes,
                         void *hip_stream) {
+  CallLog log_("moda_bwd_ws", s);
   moda_status st = bwd_check(s);
   if (st != MODA_OK) return st;
   const size_t need = bwd_ws_bytes(s);
@@ -538,6 +584,7 @@ moda_status moda_bwd_ws(const moda_shape *s, const void *q, const void *k, const
 moda_status moda_fwd_natural(const moda_shape *s, const void *q, const void *k, const void *v,
                              const void *k_depth, const void *v_depth, void *out, float *lse,
                              void *hip_stream) {
+  CallLog log_("moda_fwd_natural", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (!use_mfma(s))
@@ -570,6 +617,7 @@ size_t moda_decode_workspace_bytes(const moda_shape *s) {
 moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
                         const void *v_cache, const void *k_depth, const void *v_depth, void *out,
                         float *lse, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  CallLog log_("moda_decode", s);
   return decode_impl(s, nullptr, q, k_cache, v_cache, k_depth, v_depth, out, lse, workspace,
                      workspace_bytes, hip_stream);
 }
@@ -577,6 +625,7 @@ moda_status moda_decode(const moda_shape *s, const void *q, const void *k_cache,
 moda_status moda_decode_noalloc(const moda_shape *s, const int32_t *cache_lens, const void *q,
                                 const void *k_cache, const void *v_cache, const void *k_depth,
                                 const void *v_depth, void *out, float *lse, void *hip_stream) {
+  CallLog log_("moda_decode_noalloc", s);
   moda_status st = decode_check_args(s, q, k_cache, v_cache, k_depth, v_depth, out, lse);
   if (st != MODA_OK) return st;
   if (cache_lens && ((uintptr_t)cache_lens & 3u) != 0)
@@ -598,6 +647,7 @@ moda_status moda_decode_varlen(const moda_shape *s, const int32_t *cache_lens, c
                                const void *k_cache, const void *v_cache, const void *k_depth,
                                const void *v_depth, void *out, float *lse, void *workspace,
                                size_t workspace_bytes, void *hip_stream) {
+  CallLog log_("moda_decode_varlen", s);
   if (!cache_lens) return fail(MODA_ERR_INVALID_ARG, "cache_lens must be non-NULL");
   if (((uintptr_t)cache_lens & 3u) != 0)
     return fail(MODA_ERR_INVALID_ARG, "cache_lens must be 4-byte aligned");
@@ -609,6 +659,7 @@ moda_status moda_fwd_strided(const moda_shape *s, const void *q, const void *k, 
                              const void *k_depth, const void *v_depth, int64_t stride_bh,
                              int64_t stride_t, int64_t stride_i, void *out, float *lse,
                              void *hip_stream) {
+  CallLog log_("moda_fwd_strided", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (!use_mfma(s))
@@ -649,6 +700,7 @@ moda_status moda_fwd_strided(const moda_shape *s, const void *q, const void *k, 
 moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, const void *v,
                             const void *k_layers, const void *v_layers, void *out, float *lse,
                             void *hip_stream) {
+  CallLog log_("moda_fwd_layers", s);
   const moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   // [L, B, Hkv, T, d]: row (b, g, t, i) at (i * B * Hkv + b * Hkv + g) * T + t
@@ -659,6 +711,7 @@ moda_status moda_fwd_layers(const moda_shape *s, const void *q, const void *k, c
 moda_status moda_fwd_masked_scan(const moda_shape *s, const void *q, const void *k,
                                  const void *v, const void *k_depth, const void *v_depth,
                                  void *out, float *lse, void *hip_stream) {
+  CallLog log_("moda_fwd_masked_scan", s);
   moda_status st = moda_check_shape(s);
   if (st != MODA_OK) return st;
   if (!use_mfma(s) || s->L < 1)

@@ -33,6 +33,10 @@
  *     by abort or exception; moda_last_error() gives the detail (per thread).
  *   - Device pointers must be 16-byte aligned.
  *   - Thread safety: every call is thread-safe.
+ *   - Logging: with MODA_LOG set (to anything but "0") in the environment when
+ *     the library is first used, every call that enqueues work prints one line
+ *     to stderr as it returns: the entry point, the shape, the kernel variant
+ *     the shape selects (moda_fwd_variant) and "ok" or the error text.
  */
 #ifndef MODA_H_
 #define MODA_H_

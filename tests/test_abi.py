@@ -327,3 +327,45 @@ def test_decode_noalloc_rejects_before_launch(m):
     f32 = m.make_shape(2, 16, 4, 3000, 24, 128, "f32")
     assert m.moda_decode_noalloc(f32, None, p, p, p, p, p, p, None, None) == \
         m.MODA_ERR_UNSUPPORTED
+
+
+LOG_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from depth_wise_kv_amd import moda as m
+s = m.make_shape(1, 8, 2, 300, 6, 128, "bf16")
+p = ctypes.c_void_p(4096)
+rc = m.moda_fwd(s, None, p, p, p, m.moda_depth_cache_bytes(s), p, None, None)
+err = m.moda_last_error()
+assert rc == m.MODA_ERR_INVALID_ARG, rc
+rc = m.moda_causal_fwd(None, p, p, p, p, None, None)
+assert rc == m.MODA_ERR_INVALID_ARG, rc
+print(err)
+"""
+
+
+def run_logged(env_value):
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("MODA_LOG", None)
+    if env_value is not None:
+        env["MODA_LOG"] = env_value
+    p = subprocess.run([sys.executable, "-c", LOG_SCRIPT, ROOT], capture_output=True, text=True,
+                       env=env, timeout=120)
+    assert p.returncode == 0, p.stderr
+    return p.stdout.strip(), [l for l in p.stderr.splitlines() if l.startswith("moda: ")]
+
+
+def test_dispatch_log():
+    """MODA_LOG=1: one stderr line per call that would enqueue work, naming the
+    entry point, the shape, the kernel variant and the result; the call's own
+    error text stays what moda_last_error() returns.  Unset or "0": silent."""
+    err, lines = run_logged("1")
+    assert len(lines) == 2, lines
+    assert lines[0].startswith("moda: moda_fwd B=1 Hq=8 Hkv=2 T=300 L=6 d=128 bf16 [mfma_bf16_d128_")
+    assert lines[0].endswith(": " + err) and err
+    assert lines[1] == "moda: moda_causal_fwd (no shape): shape is NULL"
+    for v in (None, "0"):
+        err2, lines2 = run_logged(v)
+        assert lines2 == [] and err2 == err
