@@ -19,6 +19,8 @@ HBM rates.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--config long_64k] [--no-cpu-baseline]
     python bench.py --sweep            # one JSON line per sweep point (no oracle)
     python bench.py --sweep --sweep-bwd   # ... with the backward timed too
+    python bench.py --sweep --results sweep.jsonl   # ... appended to a file; a rerun skips
+                                                    # the points already there
     python bench.py --decode-sweep     # one JSON line per decode shape
     python bench.py --stack --config layer_1p5b   # a stack of layers growing the depth stream
 
